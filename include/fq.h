@@ -1,0 +1,152 @@
+/*
+ * fq.h -- C ABI of libfq, FoldQuant integer linear layers on AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the FoldQuant linear site of the vla.cpp pull request page
+ * "FoldQuant W8A8/W4A4 inference and FoldQuantVLA quantized-model converter":
+ *
+ *   prologue (the page's "act" node; OpenVINO commit lists its steps):
+ *     f  = float(x_m)                                   bf16 token, widened exactly
+ *     r  = f * (1/sqrt(mean(f^2) + eps)) * gamma'       RMSNorm with the folded gain
+ *                                                       (skipped when gamma' is NULL)
+ *     r  = r / a            (explicit smoothing, fold before; dequant-mode commit)
+ *     h  = R_b r            R_b = blockdiag(H_b)/sqrt(b), Sylvester H_b, contiguous blocks
+ *     h  = h / a            (explicit smoothing, fold after)
+ *     s_m = max|h| / qmax;  q = clamp(round_half_even(h / s_m), -qmax, qmax)
+ *   GEMM (the page's "gemm" node): acc[m][n] = sum_k q_a[m][k] * q_w[n][k] (exact int32)
+ *   epilogue: y[m][n] = bf16_rne(acc * (s_m * s_n) [+ bias[n]] [+ residual[m][n]])
+ *
+ * qmax is 127 for 8-bit codes and 7 for 4-bit codes (the page's "15 activation
+ * levels").  4-bit codes are packed two per byte with the even k in the low
+ * nibble.  Weight rows are folded into the same frame on the host by
+ * fq_pack_weights: u_n = R_b(a . w_n) (fold before) or a . R_b(w_n) (fold
+ * after), then per-row symmetric round-to-nearest-even with s_n = max|u_n|/qmax.
+ *
+ * Arithmetic of the prologue: float32 with IEEE divide and sqrt and no
+ * contraction; the RMSNorm sum of squares adds the (exact) float32 squares in
+ * float64 and mean = (float)(sum / K); the butterfly runs its stages with span
+ * 1, 2, ..., b/2 and then multiplies by (float)(1/sqrt(b)).  The epilogue runs in
+ * float32 with one round-to-nearest-even to bf16.
+ *
+ * Conventions for every entry point
+ *   - Status codes: FQ_OK on success.  On any failure the call returns a code,
+ *     sets a thread-local message (fq_last_error) that names the call, the
+ *     argument and the arithmetic, writes nothing and queues no device work.
+ *     No C++ exception crosses this ABI; nothing aborts.
+ *   - Ownership: the caller allocates and frees every buffer.  The library
+ *     allocates no device memory, never synchronises, and keeps no state other
+ *     than the error message.  Inputs are read only; outputs are overwritten.
+ *   - Device entry points are asynchronous on `stream` (a hipStream_t passed as
+ *     void*; NULL is the null stream) and take device pointers.
+ *   - Shapes: M, N >= 1; K a multiple of 64 (the MFMA depth), 64 <= K <= 65536;
+ *     hblock a power of two in [1, 256] dividing K (1 = no rotation); bits in
+ *     {4, 8} for both weights and activations (W8A8, W4A4, W4A8, W8A4).
+ *   - Alignment: bf16 rows (x, residual, y) need a 16-byte aligned base and a
+ *     leading dimension that is a multiple of 8 elements; code buffers, gamma,
+ *     ascale, scales and bias need a 16-byte aligned base.
+ *   - Inputs must be finite.  A token (or weight row) whose scale is zero, or
+ *     underflows to zero, gets all-zero codes.
+ */
+#ifndef FQ_H
+#define FQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FQ_ABI_VERSION 1
+
+typedef enum {
+    FQ_OK = 0,
+    FQ_ERR_ARG = 1,          /* NULL pointer or out-of-range scalar */
+    FQ_ERR_SHAPE = 2,        /* M, N, K, leading dimensions or hblock inconsistent */
+    FQ_ERR_UNSUPPORTED = 3,  /* a bit width or size this build does not handle */
+    FQ_ERR_ALIGN = 4,        /* pointer or leading dimension misaligned */
+    FQ_ERR_DEVICE = 5        /* a HIP call failed; the message holds hipGetErrorString */
+} fq_status;
+
+/* Message of the last failed call on this thread ("" if none).  Valid until the
+ * next fq_* call on the same thread. */
+const char* fq_last_error(void);
+
+/* FQ_ABI_VERSION of the built library. */
+int fq_abi_version(void);
+
+/* ------------------------------------------------------------------ host, synchronous */
+
+/* Bytes of one code matrix of rows x K codes at `bits` bits (rows*K or rows*K/2);
+ * 0 on bad arguments. */
+size_t fq_weight_bytes(int32_t N, int32_t K, int32_t wbits);
+size_t fq_act_bytes(int32_t M, int32_t K, int32_t abits);
+
+/* gamma_out[k] = gamma[k] / ascale[k] in float32 (host).  Norm sites carry the
+ * smoothing vector inside the RMSNorm gain (dequant-mode commit of the page).
+ * ascale NULL copies gamma. */
+fq_status fq_fold_gain(const float* gamma, const float* ascale, int32_t K, float* gamma_out);
+
+/* Host weight packer (the page's converter and bring-up export: rotation and
+ * per-row round-to-nearest, no calibration).
+ *   W          host float32 [N][K], nn.Linear layout (row n = output feature n)
+ *   ascale     host float32 [K] smoothing vector, or NULL (a = 1)
+ *   fold_after 0: u_n = R_b(a . w_n); 1: u_n = a . R_b(w_n) -- must match the
+ *              prologue's fold order (or the gain fold, which is fold before)
+ *   hblock     Hadamard block b (1 = no rotation)
+ *   codes_out  host, fq_weight_bytes(N, K, wbits) bytes: int8 [N][K] or packed [N][K/2]
+ *   wscale_out host float32 [N]: s_n = (float)(max|u_n| / qmax)
+ * The fold runs in float64; codes are rounded (ties to even) against the stored
+ * float32 scale and clamped to +-qmax. */
+fq_status fq_pack_weights(const float* W, int32_t N, int32_t K, const float* ascale,
+                          int32_t fold_after, int32_t hblock, int32_t wbits,
+                          void* codes_out, float* wscale_out);
+
+/* ------------------------------------------------------------------ device, asynchronous */
+
+/* Prologue: quantise M bf16 tokens into codes and per-token scales.
+ *   x_bf16       device bf16 [M][ldx]
+ *   gamma_folded device float32 [K] (gamma / a at norm sites) or NULL: no RMSNorm
+ *   eps          RMSNorm epsilon (ignored without gamma)
+ *   ascale       device float32 [K] explicit smoothing divide, or NULL
+ *   fold_after   0: divide before the rotation; 1: after it
+ *   act_codes    device, fq_act_bytes(M, K, abits) bytes, row stride K (or K/2) bytes
+ *   act_scale    device float32 [M] */
+fq_status fq_prologue(const void* x_bf16, int32_t M, int32_t K, int64_t ldx,
+                      const float* gamma_folded, float eps, const float* ascale,
+                      int32_t fold_after, int32_t hblock, int32_t abits,
+                      void* act_codes, float* act_scale, void* stream);
+
+/* Integer GEMM with the fused epilogue (the page's gemm node: integer GEMM,
+ * per-row weight scale, residual add).
+ *   act_codes/act_scale  device, as written by fq_prologue (row stride K or K/2 bytes)
+ *   w_codes/wscale       device, as written by fq_pack_weights
+ *   bias                 device float32 [N] or NULL
+ *   residual_bf16        device bf16 [M][ldr] or NULL
+ *   y_bf16               device bf16 [M][ldy]
+ *   acc_i32              device int32 [M][N] (row stride N) receiving the exact
+ *                        accumulators, or NULL (diagnostic output)
+ * M <= 32 runs the weight-streaming GEMV kernel, larger M the tiled MFMA kernel;
+ * both give identical results. */
+fq_status fq_gemm(const void* act_codes, const float* act_scale, int32_t M, int32_t abits,
+                  const void* w_codes, const float* wscale, int32_t N, int32_t K, int32_t wbits,
+                  const float* bias, const void* residual_bf16, int64_t ldr,
+                  void* y_bf16, int64_t ldy, int32_t* acc_i32, void* stream);
+
+/* Workspace of fq_linear: the activation codes and scales (256-byte aligned parts). */
+size_t fq_linear_workspace_bytes(int32_t M, int32_t K, int32_t abits);
+
+/* Prologue then GEMM on one stream; arguments as in fq_prologue and fq_gemm.
+ * workspace: device, at least fq_linear_workspace_bytes(M, K, abits) bytes,
+ * 256-byte aligned; it holds the codes and scales after the call. */
+fq_status fq_linear(const void* x_bf16, int32_t M, int32_t K, int64_t ldx,
+                    const float* gamma_folded, float eps, const float* ascale,
+                    int32_t fold_after, int32_t hblock, int32_t abits,
+                    const void* w_codes, const float* wscale, int32_t N, int32_t wbits,
+                    const float* bias, const void* residual_bf16, int64_t ldr,
+                    void* y_bf16, int64_t ldy,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FQ_H */

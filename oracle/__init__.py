@@ -29,7 +29,7 @@ from .build import LIB, build
 __all__ = [
     "lib", "hadamard_entry", "rotate_f64", "butterfly_f32", "fold_gain", "fold_weights",
     "pack_weights", "unfold_weights", "act_frame", "prologue", "gemm_i32", "epilogue",
-    "bf16_from_f64", "code_at", "unpack_codes", "linear", "row_bytes", "qmax",
+    "bf16_from_f64", "code_at", "num_threads", "unpack_codes", "linear", "row_bytes", "qmax",
 ]
 
 _lib = None
@@ -61,6 +61,7 @@ def lib():
         L.fqo_bf16_from_f64.argtypes = [ctypes.c_double]
         L.fqo_bf16_from_f64.restype = ctypes.c_uint16
         L.fqo_code_at.argtypes = [_P, _I32, _I32]
+        L.fqo_num_threads.argtypes = []
         _lib = L
     return _lib
 
@@ -206,6 +207,11 @@ def epilogue(acc, act_scale, wscale, bias=None, residual_bits=None, want_f64: bo
 def bf16_from_f64(v: float) -> int:
     """Nearest-even bfloat16 bits of a float64 (one rounding)."""
     return int(lib().fqo_bf16_from_f64(float(v)))
+
+
+def num_threads() -> int:
+    """Threads the oracle's OpenMP loops use."""
+    return int(lib().fqo_num_threads())
 
 
 def code_at(row: np.ndarray, k: int, bits: int) -> int:

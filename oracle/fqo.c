@@ -22,6 +22,9 @@
 #include "fqo.h"
 
 #include <math.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 #include <stdlib.h>
 #include <string.h>
 
@@ -312,4 +315,12 @@ int fqo_epilogue(const int32_t* acc, int32_t M, int32_t N, const float* act_scal
             y[(int64_t)m * N + n] = fqo_bf16_from_f64(t);
         }
     return 0;
+}
+
+int fqo_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
 }

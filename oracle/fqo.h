@@ -97,6 +97,9 @@ int fqo_epilogue(const int32_t* acc, int32_t M, int32_t N, const float* act_scal
 /* Nearest-even bfloat16 of a float64 value (one rounding). */
 uint16_t fqo_bf16_from_f64(double v);
 
+/* Threads the oracle's parallel loops use (OpenMP max threads). */
+int fqo_num_threads(void);
+
 /* Integer value of code k of a row (int8 or packed 4-bit). */
 int32_t fqo_code_at(const void* row, int32_t k, int32_t bits);
 

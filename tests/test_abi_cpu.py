@@ -1,0 +1,206 @@
+"""CPU-only checks of libfq: it loads, exports every symbol include/fq.h declares,
+its host packer and gain fold match the oracle bit for bit, and every device
+entry point rejects bad arguments before touching the GPU (the page's
+convention: refuse an impossible request up front, naming the argument and
+the arithmetic)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+import w4a4_integer_gemm_amd as fq
+from w4a4_integer_gemm_amd import _binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fq.h")
+
+# a fake but aligned "device pointer": validation never dereferences it
+DEV = 0x10000
+BAD = 0x10001
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = fq.lib()
+    names = header_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(_binding.SIGNATURES), "binding and header disagree"
+    assert fq.abi_version() == 1
+
+
+def test_sizes():
+    assert fq.fq_weight_bytes(4608, 3584, 8) == 4608 * 3584
+    assert fq.fq_weight_bytes(32768, 2048, 4) == 32768 * 1024
+    assert fq.fq_act_bytes(816, 16384, 4) == 816 * 8192
+    assert fq.fq_weight_bytes(0, 64, 8) == 0 and fq.fq_weight_bytes(4, 64, 3) == 0
+    ws = fq.fq_linear_workspace_bytes(1024, 3584, 8)
+    assert ws >= 1024 * 3584 + 4 * 1024 and ws % 256 == 0
+
+
+@pytest.mark.parametrize("wbits", [8, 4])
+@pytest.mark.parametrize("fold_after", [0, 1])
+@pytest.mark.parametrize("hblock", [1, 2, 8, 32, 64, 128, 256])
+@pytest.mark.parametrize("with_a", [False, True])
+def test_host_packer_matches_oracle(wbits, fold_after, hblock, with_a):
+    rng = np.random.default_rng(hblock * 7 + wbits + fold_after)
+    N, K = 24, 512
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    W[:, 7] *= 50
+    W[3] = 0.0  # an all-zero row: scale 0, codes 0
+    a = rng.uniform(0.15, 6.4, K).astype(np.float32) if with_a else None
+    c1, s1 = fq.fq_pack_weights(W, a, fold_after, hblock, wbits)
+    c2, s2 = oracle.pack_weights(W, a, fold_after, hblock, wbits)
+    assert np.array_equal(s1, s2)
+    assert np.array_equal(c1, c2)
+    assert s1[3] == 0 and np.all(c1[3] == 0)
+
+
+def test_host_packer_matches_oracle_on_workload_shapes():
+    wl = synth.make_workload("qkv_w8a8", N=256)
+    c1, s1 = fq.fq_pack_weights(wl.W, wl.ascale, 0, wl.hblock, 8)
+    c2, s2 = oracle.pack_weights(wl.W, wl.ascale, 0, wl.hblock, 8)
+    assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
+    wl = synth.make_workload("gateup_w4a4", N=256)
+    c1, s1 = fq.fq_pack_weights(wl.W, wl.ascale, 0, wl.hblock, 4)
+    c2, s2 = oracle.pack_weights(wl.W, wl.ascale, 0, wl.hblock, 4)
+    assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
+
+
+def test_fold_gain_matches_oracle():
+    rng = np.random.default_rng(1)
+    g = rng.uniform(0.5, 1.5, 3584).astype(np.float32)
+    a = rng.uniform(0.1, 160.0, 3584).astype(np.float32)
+    assert np.array_equal(fq.fq_fold_gain(g, a), oracle.fold_gain(g, a))
+    assert np.array_equal(fq.fq_fold_gain(g, None), g)
+    with pytest.raises(fq.FqError, match="ascale\\[2\\]"):
+        a2 = a.copy()
+        a2[2] = 0
+        fq.fq_fold_gain(g, a2)
+
+
+@pytest.mark.parametrize("kw,match", [
+    (dict(wbits=3), "wbits=3"),
+    (dict(K=100), "K=100"),
+    (dict(K=192, hblock=128), r"K=192 not divisible by hblock=128 \(192/128 = 1.50\)"),
+    (dict(hblock=3), "hblock=3"),
+    (dict(hblock=512), "hblock=512"),
+    (dict(fold_after=2), "fold_after=2"),
+])
+def test_host_packer_rejects(kw, match):
+    args = dict(N=4, K=256, hblock=64, wbits=8, fold_after=0)
+    args.update(kw)
+    W = np.zeros((args["N"], args["K"]), np.float32)
+    with pytest.raises(fq.FqError, match=match):
+        fq.fq_pack_weights(W, None, args["fold_after"], args["hblock"], args["wbits"])
+
+
+def _prologue(**kw):
+    a = dict(x=DEV, M=4, K=256, ldx=256, gamma=DEV, eps=1e-6, ascale=None, fold_after=0, hblock=64, abits=8,
+             codes=DEV, scale=DEV)
+    a.update(kw)
+    L = fq.lib()
+    return L.fq_prologue(a["x"], a["M"], a["K"], a["ldx"], a["gamma"], a["eps"], a["ascale"], a["fold_after"],
+                         a["hblock"], a["abits"], a["codes"], a["scale"], None)
+
+
+@pytest.mark.parametrize("kw,status,match", [
+    (dict(x=None), 1, "x_bf16 is NULL"),
+    (dict(codes=None), 1, "act_codes is NULL"),
+    (dict(scale=None), 1, "act_scale is NULL"),
+    (dict(M=0), 2, "M=0"),
+    (dict(K=96, ldx=96), 2, r"K=96 is not a multiple of the MFMA depth 64 \(96/64 = 1.50\)"),
+    (dict(K=131072, ldx=131072), 2, "K=131072 outside"),
+    (dict(hblock=48), 2, "hblock=48"),
+    (dict(K=320, ldx=320, hblock=128), 2, r"K=320 not divisible by hblock=128 \(320/128 = 2.50\)"),
+    (dict(abits=2), 3, "abits=2"),
+    (dict(ldx=255), 2, "ldx=255 < K=256"),
+    (dict(ldx=260), 4, "ldx=260 is not a multiple of 8"),
+    (dict(x=BAD), 4, "x_bf16 is not 16-byte aligned"),
+    (dict(codes=BAD), 4, "act_codes is not 16-byte aligned"),
+    (dict(fold_after=5), 1, "fold_after=5"),
+    (dict(eps=float("nan")), 1, "eps=nan"),
+])
+def test_prologue_rejects_before_device_work(kw, status, match):
+    rc = _prologue(**kw)
+    assert rc == status
+    msg = fq.last_error()
+    assert msg.startswith("fq_prologue:")
+    assert re.search(match, msg), msg
+
+
+def _gemm(**kw):
+    a = dict(act=DEV, sa=DEV, M=64, abits=8, w=DEV, sw=DEV, N=128, K=256, wbits=8, bias=None, res=None, ldr=0,
+             y=DEV, ldy=128, acc=None)
+    a.update(kw)
+    return fq.lib().fq_gemm(a["act"], a["sa"], a["M"], a["abits"], a["w"], a["sw"], a["N"], a["K"], a["wbits"],
+                            a["bias"], a["res"], a["ldr"], a["y"], a["ldy"], a["acc"], None)
+
+
+@pytest.mark.parametrize("kw,status,match", [
+    (dict(w=None), 1, "w_codes is NULL"),
+    (dict(y=None), 1, "y_bf16 is NULL"),
+    (dict(N=0), 2, "N=0"),
+    (dict(N=100, ldy=100), 2, r"N=100 is not a multiple of 8 \(100/8 = 12.500\)"),
+    (dict(ldy=64), 2, "ldy=64 < N=128"),
+    (dict(res=DEV, ldr=64), 2, "ldr=64 < N=128"),
+    (dict(res=DEV, ldr=132), 4, "ldr=132 is not a multiple of 8"),
+    (dict(wbits=6), 3, "wbits=6"),
+    (dict(w=BAD), 4, "w_codes is not 16-byte aligned"),
+    (dict(acc=BAD), 4, "acc_i32 is not 16-byte aligned"),
+    (dict(K=0), 2, "K=0"),
+])
+def test_gemm_rejects_before_device_work(kw, status, match):
+    rc = _gemm(**kw)
+    assert rc == status
+    msg = fq.last_error()
+    assert msg.startswith("fq_gemm:") and re.search(match, msg), msg
+
+
+def _linear(**kw):
+    a = dict(x=DEV, M=16, K=256, ldx=256, gamma=DEV, eps=1e-6, ascale=None, fold_after=0, hblock=64, abits=8,
+             w=DEV, sw=DEV, N=128, wbits=8, bias=None, res=None, ldr=0, y=DEV, ldy=128, ws=0x100000,
+             wsb=1 << 20)
+    a.update(kw)
+    return fq.lib().fq_linear(a["x"], a["M"], a["K"], a["ldx"], a["gamma"], a["eps"], a["ascale"], a["fold_after"],
+                              a["hblock"], a["abits"], a["w"], a["sw"], a["N"], a["wbits"], a["bias"], a["res"],
+                              a["ldr"], a["y"], a["ldy"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status,match", [
+    (dict(ws=None), 1, "workspace is NULL"),
+    (dict(ws=0x100010), 4, "workspace is not 256-byte aligned"),
+    (dict(wsb=100), 1, r"workspace_bytes=100 < \d+ needed for M=16 K=256 abits=8"),
+    (dict(hblock=7), 2, "hblock=7"),
+    (dict(N=12, ldy=16), 2, "N=12 is not a multiple of 8"),
+    (dict(abits=5), 3, "abits=5"),
+])
+def test_linear_rejects_before_device_work(kw, status, match):
+    rc = _linear(**kw)
+    assert rc == status
+    msg = fq.last_error()
+    assert msg.startswith("fq_linear:") and re.search(match, msg), msg
+
+
+def test_error_message_is_cleared_by_a_good_host_call():
+    _gemm(N=0)
+    assert fq.last_error()
+    fq.fq_pack_weights(np.ones((2, 64), np.float32), None, 0, 64, 8)
+    assert fq.last_error() == ""
+
+
+def test_binding_refuses_host_tensors_for_device_calls():
+    import torch
+    with pytest.raises(ValueError, match="GPU tensors"):
+        fq.fq_prologue(torch.zeros(4, 64, dtype=torch.int16), 4, 64, 64, None, 1e-6, None, 0, 64, 8,
+                       torch.zeros(256, dtype=torch.uint8), torch.zeros(4), None)

@@ -1,0 +1,85 @@
+"""GPU parity of fq_gemm (tiled MFMA kernel for M > 32, weight-streaming GEMV for
+M <= 32) on identical codes: the int32 accumulators must equal the oracle's
+bit for bit (the SYCL commit of the vla.cpp FoldQuant page: integer sums are
+exact in any order), and each bf16 output must sit within the epilogue's
+rounding bound of the oracle's float64 value."""
+import numpy as np
+import pytest
+
+import oracle
+from fqtest import assert_y_elementwise, dev, host, log
+
+pytestmark = pytest.mark.gpu
+
+
+def rand_codes(rng, rows, K, bits, extreme=False):
+    qmax = oracle.qmax(bits)
+    if extreme:
+        q = rng.choice([-qmax, qmax], size=(rows, K))
+    else:
+        q = rng.integers(-qmax, qmax + 1, size=(rows, K))
+    if bits == 8:
+        return q.astype(np.int8).view(np.uint8)
+    return ((q[:, 0::2] & 0xF) | ((q[:, 1::2] & 0xF) << 4)).astype(np.uint8)
+
+
+def run_gemm(M, N, K, abits, wbits, seed, bias=False, residual=False, extreme=False, ldy=None, ldr=None):
+    rng = np.random.default_rng(seed)
+    ca = rand_codes(rng, M, K, abits, extreme)
+    cw = rand_codes(rng, N, K, wbits, extreme)
+    sa = rng.uniform(0.001, 0.05, M).astype(np.float32)
+    sw = rng.uniform(0.0001, 0.002, N).astype(np.float32)
+    b = (rng.standard_normal(N) * 0.1).astype(np.float32) if bias else None
+    ldr = ldr or N
+    res = None
+    if residual:
+        res = np.zeros((M, ldr), np.uint16)
+        res[:, :N] = (rng.standard_normal((M, N)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    acc_ref = oracle.gemm_i32(ca, abits, cw, wbits, K)
+    y_ref, yf = oracle.epilogue(acc_ref, sa, sw, b, None if res is None else res[:, :N], want_f64=True)
+    ldy = ldy or N
+    y = dev(np.zeros((M, ldy), np.uint16))
+    acc = dev(np.zeros((M, N), np.int32))
+    from w4a4_integer_gemm_amd import fq_gemm
+    fq_gemm(dev(ca), dev(sa), M, abits, dev(cw), dev(sw), N, K, wbits, None if b is None else dev(b),
+            None if res is None else dev(res), ldr, y, ldy, acc)
+    yg = host(y, np.uint16)[:, :N]
+    return host(acc), acc_ref, yg, yf, sa, sw, b, None if res is None else res[:, :N]
+
+
+SHAPES = [
+    # M, N, K  (M <= 32 takes the GEMV kernel)
+    (1, 8, 64), (1, 520, 3584), (5, 136, 192), (16, 512, 256), (17, 264, 640), (32, 1000, 1024),
+    (33, 8, 64), (33, 136, 192), (64, 128, 128), (100, 392, 704), (128, 256, 3584), (130, 520, 256),
+    (300, 1000, 2048), (816, 264, 1024),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "M{}_N{}_K{}".format(*s))
+@pytest.mark.parametrize("bits", [(8, 8), (4, 4), (8, 4), (4, 8)], ids=lambda b: "A{}W{}".format(*b))
+def test_gemm_bit_exact_on_identical_codes(shape, bits):
+    M, N, K = shape
+    abits, wbits = bits
+    log(f"gemm M={M} N={N} K={K} A{abits}W{wbits}")
+    acc, acc_ref, yg, yf, sa, sw, b, res = run_gemm(M, N, K, abits, wbits, seed=M * 7 + N + K + abits,
+                                                    bias=(M % 2 == 1), residual=(N % 16 == 8))
+    assert np.array_equal(acc, acc_ref), f"{np.count_nonzero(acc != acc_ref)} accumulators differ"
+    assert_y_elementwise(yg, yf, acc_ref, sa, sw, b, res, what=f"M{M} N{N} K{K}")
+
+
+@pytest.mark.parametrize("M", [16, 256])
+@pytest.mark.parametrize("bits", [(8, 8), (4, 4)], ids=lambda b: "A{}W{}".format(*b))
+def test_gemm_extreme_codes_longest_row(M, bits):
+    """Every code at +-qmax on K = 18944 (the largest accumulator of the workloads)."""
+    log(f"gemm extreme codes M={M} bits={bits}")
+    acc, acc_ref, yg, yf, sa, sw, b, res = run_gemm(M, 256, 18944, bits[0], bits[1], seed=5, extreme=True)
+    assert np.array_equal(acc, acc_ref)
+    assert_y_elementwise(yg, yf, acc_ref, sa, sw, what="extreme")
+
+
+def test_gemm_strided_output_and_residual():
+    log("gemm strided ldy/ldr")
+    for M in (8, 200):
+        acc, acc_ref, yg, yf, sa, sw, b, res = run_gemm(M, 136, 256, 8, 8, seed=9, residual=True, ldy=144, ldr=152)
+        assert np.array_equal(acc, acc_ref)
+        assert_y_elementwise(yg, yf, acc_ref, sa, sw, None, res, what=f"strided M={M}")

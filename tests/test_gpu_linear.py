@@ -1,0 +1,87 @@
+"""End-to-end GPU parity of fq_linear (prologue + GEMM/GEMV + epilogue) against
+the oracle, on the option matrix of the vla.cpp FoldQuant page's SYCL test
+(gamma, ascale before/after, bias, residual, narrowed and no rotation, the four
+precisions) and on the five workloads at their full sizes (sampled tokens)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+import w4a4_integer_gemm_amd as fq
+from fqtest import assert_codes, assert_y_elementwise, assert_y_fro, dev, host, log
+
+pytestmark = pytest.mark.gpu
+
+
+def site_for(wl):
+    return fq.DeviceSite(wl.W, wl.hblock, wl.wbits, wl.abits, gamma=wl.gamma, ascale=wl.ascale,
+                         fold_after=wl.fold_after, fold_into_gain=wl.fold_into_gain, bias=wl.bias, eps=wl.eps)
+
+
+def check_linear(wl, site, rows=None, what=""):
+    """Run fq_linear on all M tokens; check the given token rows against the oracle."""
+    M = wl.M
+    x = dev(wl.x)
+    res = dev(wl.residual) if wl.residual is not None else None
+    y = site.linear(x, residual=res)
+    codes_d, scales_d = site.workspace_codes(M)
+    yg = host(y, np.uint16)
+    gcodes = host(codes_d).reshape(M, -1)
+    gscale = host(scales_d)
+    rows = np.arange(M) if rows is None else np.asarray(rows)
+    # oracle on the sampled tokens, with the product packer's codes (checked equal to
+    # the oracle packer by the CPU tests)
+    sub = synth.Workload(**{**wl.__dict__, "x": wl.x[rows], "M": len(rows),
+                            "residual": None if wl.residual is None else wl.residual[rows]})
+    out = oracle.linear(sub, codes_w=site.codes_host, wscale=site.wscale_host)
+    frac = assert_codes(gcodes[rows], gscale[rows], out["codes_a"], out["act_scale"], wl.K, wl.abits, what=what)
+    assert_y_fro(yg[rows], out["y_f64"], what=what)
+    # tokens whose codes all agree must meet the element-wise epilogue bound
+    same = np.all(gcodes[rows] == out["codes_a"], axis=1) & (gscale[rows] == out["act_scale"])
+    if np.any(same):
+        r = np.nonzero(same)[0]
+        assert_y_elementwise(yg[rows][r], out["y_f64"][r], out["acc"][r], out["act_scale"][r], out["wscale"],
+                             wl.bias, None if wl.residual is None else wl.residual[rows][r], what=what + " same-codes")
+    return frac
+
+
+OPTION_CASES = [
+    # M, K, N, hblock, wbits, abits, norm, ascale, fold_after, bias, residual
+    (16, 256, 512, 64, 8, 8, True, "gain", 0, False, False),
+    (1, 512, 264, 128, 8, 8, True, "gain", 0, True, False),
+    (32, 1024, 520, 32, 4, 4, True, "explicit", 1, False, True),
+    (33, 2048, 392, 128, 4, 4, False, "none", 0, True, True),
+    (300, 2048, 256, 1, 8, 8, True, "none", 0, False, False),      # no rotation
+    (300, 6144, 136, 16, 4, 8, False, "explicit", 0, True, False),  # W4A8, narrowed block
+    (70, 16384, 128, 128, 8, 4, True, "gain", 0, False, True),      # W8A4
+    (129, 1024, 1000, 256, 8, 8, False, "explicit", 1, True, True),
+]
+
+
+@pytest.mark.parametrize("case", OPTION_CASES, ids=lambda c: "M{}_K{}_N{}_b{}_W{}A{}_{}".format(*c[:7]))
+def test_linear_option_matrix(case):
+    M, K, N, b, wb, ab, norm, amode, fa, bias, resid = case
+    log(f"linear option case {case}")
+    wl = synth.random_workload(M, K, N, b, wb, ab, seed=M + K + N, norm=norm, ascale=amode, fold_after=fa,
+                               bias=bias, residual=resid)
+    check_linear(wl, site_for(wl), what=str(case))
+
+
+def test_linear_tiny_workload_full():
+    wl = synth.make_workload("tiny_w8a8")
+    log("linear tiny_w8a8 (16x256x512)")
+    check_linear(wl, site_for(wl), what="tiny_w8a8")
+
+
+@pytest.mark.parametrize("name", ["qkv_w8a8", "down_w8a8", "decode_m1_w8a8", "decode_m16_w8a8", "gateup_w4a4",
+                                  "down_w4a4"])
+def test_linear_workload_full_size_sampled(name):
+    """Full-size workload through fq_linear in the benchmark's launch configuration;
+    the oracle recomputes a sample of tokens (all output features of each)."""
+    log(f"linear workload {name}: building inputs")
+    wl = synth.make_workload(name)
+    site = site_for(wl)
+    rng = np.random.default_rng(1)
+    rows = np.unique(np.concatenate([[0, wl.M - 1], rng.choice(wl.M, size=min(wl.M, 24), replace=False)]))
+    log(f"linear workload {name}: M={wl.M} K={wl.K} N={wl.N} rows checked {len(rows)}")
+    check_linear(wl, site, rows=rows, what=name)

@@ -1,0 +1,16 @@
+"""FoldQuant W8A8/W4A4 integer linear layers for AMD Instinct MI355X (gfx950).
+
+The layer (the vla.cpp FoldQuant page's act + gemm nodes) runs in libfq.so:
+hand-written HIP kernels behind the C ABI declared in include/fq.h.  This
+package only loads that library and marshals arguments; torch provides device
+memory and streams.
+"""
+from ._binding import (FqError, abi_version, fq_act_bytes, fq_fold_gain, fq_gemm, fq_linear,
+                       fq_linear_workspace_bytes, fq_pack_weights, fq_prologue, fq_weight_bytes, last_error,
+                       lib)
+from .site import DeviceSite
+
+__all__ = [
+    "FqError", "abi_version", "fq_act_bytes", "fq_fold_gain", "fq_gemm", "fq_linear", "fq_linear_workspace_bytes",
+    "fq_pack_weights", "fq_prologue", "fq_weight_bytes", "last_error", "lib", "DeviceSite",
+]

@@ -1,0 +1,239 @@
+// C ABI of libfq: argument validation, error messages and kernel dispatch.
+//
+// Every check runs before any HIP call, so a rejected call queues no device
+// work and writes nothing.  The messages follow the page's convention of
+// naming the call and argument and showing the arithmetic that failed.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "../../include/fq.h"
+#include "fq_internal.h"
+
+namespace fq {
+
+static thread_local std::string g_error;
+
+void set_error(const std::string& msg) { g_error = msg; }
+void clear_error() { g_error.clear(); }
+
+}  // namespace fq
+
+namespace {
+
+std::string fmt(const char* f, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, f);
+    vsnprintf(buf, sizeof(buf), f, ap);
+    va_end(ap);
+    return std::string(buf);
+}
+
+fq_status fail(fq_status s, const std::string& msg) {
+    fq::set_error(msg);
+    return s;
+}
+
+bool is_pow2(int64_t v) { return v >= 1 && (v & (v - 1)) == 0; }
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr int32_t kMaxK = 65536;
+
+// Checks shared by the prologue, the GEMM and the packer.  Returns FQ_OK or the failure.
+fq_status check_bits(const char* fn, const char* name, int32_t bits) {
+    if (bits != 8 && bits != 4)
+        return fail(FQ_ERR_UNSUPPORTED, fmt("%s: %s=%d is not a supported code width (4 or 8)", fn, name, bits));
+    return FQ_OK;
+}
+
+fq_status check_k(const char* fn, int32_t K) {
+    if (K < 64 || K > kMaxK)
+        return fail(FQ_ERR_SHAPE, fmt("%s: K=%d outside [64, %d]", fn, K, kMaxK));
+    if (K % 64)
+        return fail(FQ_ERR_SHAPE, fmt("%s: K=%d is not a multiple of the MFMA depth 64 (%d/64 = %.2f)",
+                                      fn, K, K, K / 64.0));
+    return FQ_OK;
+}
+
+fq_status check_hblock(const char* fn, int32_t K, int32_t hblock) {
+    if (!is_pow2(hblock) || hblock > 256)
+        return fail(FQ_ERR_SHAPE, fmt("%s: hblock=%d must be a power of two in [1, 256]", fn, hblock));
+    if (K % hblock)
+        return fail(FQ_ERR_SHAPE, fmt("%s: K=%d not divisible by hblock=%d (%d/%d = %.2f)", fn, K, hblock,
+                                      K, hblock, double(K) / hblock));
+    return FQ_OK;
+}
+
+#define FQ_TRY(expr)                     \
+    do {                                 \
+        fq_status _s = (expr);           \
+        if (_s != FQ_OK) return _s;      \
+    } while (0)
+
+fq_status validate_prologue(const char* fn, const void* x, int32_t M, int32_t K, int64_t ldx,
+                            const float* gamma, float eps, const float* ascale, int32_t fold_after,
+                            int32_t hblock, int32_t abits, const void* codes, const float* scale) {
+    if (!x) return fail(FQ_ERR_ARG, fmt("%s: x_bf16 is NULL", fn));
+    if (!codes) return fail(FQ_ERR_ARG, fmt("%s: act_codes is NULL", fn));
+    if (!scale) return fail(FQ_ERR_ARG, fmt("%s: act_scale is NULL", fn));
+    if (M < 1) return fail(FQ_ERR_SHAPE, fmt("%s: M=%d must be >= 1", fn, M));
+    FQ_TRY(check_k(fn, K));
+    FQ_TRY(check_bits(fn, "abits", abits));
+    FQ_TRY(check_hblock(fn, K, hblock));
+    if (ldx < K) return fail(FQ_ERR_SHAPE, fmt("%s: ldx=%lld < K=%d", fn, (long long)ldx, K));
+    if (ldx % 8) return fail(FQ_ERR_ALIGN, fmt("%s: ldx=%lld is not a multiple of 8 bf16 (16 bytes)", fn, (long long)ldx));
+    if (fold_after != 0 && fold_after != 1)
+        return fail(FQ_ERR_ARG, fmt("%s: fold_after=%d must be 0 or 1", fn, fold_after));
+    if (gamma && !(eps >= 0.0f && eps < 1e30f))
+        return fail(FQ_ERR_ARG, fmt("%s: eps=%g must be finite and >= 0", fn, (double)eps));
+    if (!aligned(x, 16)) return fail(FQ_ERR_ALIGN, fmt("%s: x_bf16 is not 16-byte aligned", fn));
+    if (!aligned(codes, 16)) return fail(FQ_ERR_ALIGN, fmt("%s: act_codes is not 16-byte aligned", fn));
+    if (!aligned(scale, 4)) return fail(FQ_ERR_ALIGN, fmt("%s: act_scale is not 4-byte aligned", fn));
+    if (gamma && !aligned(gamma, 16)) return fail(FQ_ERR_ALIGN, fmt("%s: gamma_folded is not 16-byte aligned", fn));
+    if (ascale && !aligned(ascale, 16)) return fail(FQ_ERR_ALIGN, fmt("%s: ascale is not 16-byte aligned", fn));
+    return FQ_OK;
+}
+
+fq_status validate_gemm(const char* fn, const void* act, const float* act_scale, int32_t M, int32_t abits,
+                        const void* w, const float* wscale, int32_t N, int32_t K, int32_t wbits,
+                        const float* bias, const void* residual, int64_t ldr, const void* y, int64_t ldy,
+                        bool check_act) {
+    if (check_act && !act) return fail(FQ_ERR_ARG, fmt("%s: act_codes is NULL", fn));
+    if (check_act && !act_scale) return fail(FQ_ERR_ARG, fmt("%s: act_scale is NULL", fn));
+    if (!w) return fail(FQ_ERR_ARG, fmt("%s: w_codes is NULL", fn));
+    if (!wscale) return fail(FQ_ERR_ARG, fmt("%s: wscale is NULL", fn));
+    if (!y) return fail(FQ_ERR_ARG, fmt("%s: y_bf16 is NULL", fn));
+    if (M < 1) return fail(FQ_ERR_SHAPE, fmt("%s: M=%d must be >= 1", fn, M));
+    if (N < 1) return fail(FQ_ERR_SHAPE, fmt("%s: N=%d must be >= 1", fn, N));
+    if (N % 8) return fail(FQ_ERR_SHAPE, fmt("%s: N=%d is not a multiple of 8 (%d/8 = %.3f)", fn, N, N, N / 8.0));
+    FQ_TRY(check_k(fn, K));
+    FQ_TRY(check_bits(fn, "abits", abits));
+    FQ_TRY(check_bits(fn, "wbits", wbits));
+    if (ldy < N) return fail(FQ_ERR_SHAPE, fmt("%s: ldy=%lld < N=%d", fn, (long long)ldy, N));
+    if (ldy % 8) return fail(FQ_ERR_ALIGN, fmt("%s: ldy=%lld is not a multiple of 8 bf16", fn, (long long)ldy));
+    if (residual && ldr < N) return fail(FQ_ERR_SHAPE, fmt("%s: ldr=%lld < N=%d", fn, (long long)ldr, N));
+    if (residual && ldr % 8) return fail(FQ_ERR_ALIGN, fmt("%s: ldr=%lld is not a multiple of 8 bf16", fn, (long long)ldr));
+    if (check_act && !aligned(act, 16)) return fail(FQ_ERR_ALIGN, fmt("%s: act_codes is not 16-byte aligned", fn));
+    if (check_act && !aligned(act_scale, 4)) return fail(FQ_ERR_ALIGN, fmt("%s: act_scale is not 4-byte aligned", fn));
+    if (!aligned(w, 16)) return fail(FQ_ERR_ALIGN, fmt("%s: w_codes is not 16-byte aligned", fn));
+    if (!aligned(wscale, 16)) return fail(FQ_ERR_ALIGN, fmt("%s: wscale is not 16-byte aligned", fn));
+    if (bias && !aligned(bias, 16)) return fail(FQ_ERR_ALIGN, fmt("%s: bias is not 16-byte aligned", fn));
+    if (residual && !aligned(residual, 16)) return fail(FQ_ERR_ALIGN, fmt("%s: residual_bf16 is not 16-byte aligned", fn));
+    if (!aligned(y, 16)) return fail(FQ_ERR_ALIGN, fmt("%s: y_bf16 is not 16-byte aligned", fn));
+    return FQ_OK;
+}
+
+fq_status device_status(const char* fn, hipError_t e) {
+    if (e != hipSuccess) return fail(FQ_ERR_DEVICE, fmt("%s: %s", fn, hipGetErrorString(e)));
+    return FQ_OK;
+}
+
+size_t code_bytes(int32_t rows, int32_t K, int32_t bits) {
+    if (rows < 1 || K < 2 || K % 2 || (bits != 4 && bits != 8)) return 0;
+    return bits == 8 ? size_t(rows) * size_t(K) : size_t(rows) * size_t(K / 2);
+}
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+fq_status run_gemm(const char* fn, const fq::GemmArgs& g, hipStream_t stream) {
+    hipError_t e = g.M <= fq::kGemvMaxM ? fq::launch_gemv(g, stream) : fq::launch_gemm(g, stream);
+    return device_status(fn, e);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fq_last_error(void) { return fq::g_error.c_str(); }
+
+int fq_abi_version(void) { return FQ_ABI_VERSION; }
+
+size_t fq_weight_bytes(int32_t N, int32_t K, int32_t wbits) { return code_bytes(N, K, wbits); }
+
+size_t fq_act_bytes(int32_t M, int32_t K, int32_t abits) { return code_bytes(M, K, abits); }
+
+size_t fq_linear_workspace_bytes(int32_t M, int32_t K, int32_t abits) {
+    size_t c = code_bytes(M, K, abits);
+    if (!c) return 0;
+    return round_up(c, 256) + round_up(size_t(M) * sizeof(float), 256);
+}
+
+fq_status fq_fold_gain(const float* gamma, const float* ascale, int32_t K, float* gamma_out) {
+    fq::clear_error();
+    if (!gamma || !gamma_out) return fail(FQ_ERR_ARG, "fq_fold_gain: gamma or gamma_out is NULL");
+    if (K < 1) return fail(FQ_ERR_SHAPE, fmt("fq_fold_gain: K=%d must be >= 1", K));
+    if (ascale) {
+        for (int32_t k = 0; k < K; ++k)
+            if (!(ascale[k] > 0.0f))
+                return fail(FQ_ERR_ARG, fmt("fq_fold_gain: ascale[%d]=%g must be > 0", k, (double)ascale[k]));
+    }
+    for (int32_t k = 0; k < K; ++k) gamma_out[k] = ascale ? gamma[k] / ascale[k] : gamma[k];
+    return FQ_OK;
+}
+
+fq_status fq_prologue(const void* x_bf16, int32_t M, int32_t K, int64_t ldx, const float* gamma_folded,
+                      float eps, const float* ascale, int32_t fold_after, int32_t hblock, int32_t abits,
+                      void* act_codes, float* act_scale, void* stream) {
+    fq::clear_error();
+    const char* fn = "fq_prologue";
+    FQ_TRY(validate_prologue(fn, x_bf16, M, K, ldx, gamma_folded, eps, ascale, fold_after, hblock, abits,
+                             act_codes, act_scale));
+    fq::PrologueArgs a{static_cast<const uint16_t*>(x_bf16), M, K, ldx, gamma_folded, eps, ascale,
+                       fold_after, hblock, abits, static_cast<uint8_t*>(act_codes), act_scale};
+    return device_status(fn, fq::launch_prologue(a, static_cast<hipStream_t>(stream)));
+}
+
+fq_status fq_gemm(const void* act_codes, const float* act_scale, int32_t M, int32_t abits, const void* w_codes,
+                  const float* wscale, int32_t N, int32_t K, int32_t wbits, const float* bias,
+                  const void* residual_bf16, int64_t ldr, void* y_bf16, int64_t ldy, int32_t* acc_i32,
+                  void* stream) {
+    fq::clear_error();
+    const char* fn = "fq_gemm";
+    FQ_TRY(validate_gemm(fn, act_codes, act_scale, M, abits, w_codes, wscale, N, K, wbits, bias, residual_bf16,
+                         ldr, y_bf16, ldy, true));
+    if (acc_i32 && !aligned(acc_i32, 16)) return fail(FQ_ERR_ALIGN, "fq_gemm: acc_i32 is not 16-byte aligned");
+    fq::GemmArgs g{static_cast<const uint8_t*>(act_codes), act_scale, M, abits,
+                   static_cast<const uint8_t*>(w_codes), wscale, N, K, wbits, bias,
+                   static_cast<const uint16_t*>(residual_bf16), ldr, static_cast<uint16_t*>(y_bf16), ldy,
+                   acc_i32};
+    return run_gemm(fn, g, static_cast<hipStream_t>(stream));
+}
+
+fq_status fq_linear(const void* x_bf16, int32_t M, int32_t K, int64_t ldx, const float* gamma_folded, float eps,
+                    const float* ascale, int32_t fold_after, int32_t hblock, int32_t abits, const void* w_codes,
+                    const float* wscale, int32_t N, int32_t wbits, const float* bias, const void* residual_bf16,
+                    int64_t ldr, void* y_bf16, int64_t ldy, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+    fq::clear_error();
+    const char* fn = "fq_linear";
+    if (!workspace) return fail(FQ_ERR_ARG, "fq_linear: workspace is NULL");
+    if (!aligned(workspace, 256)) return fail(FQ_ERR_ALIGN, "fq_linear: workspace is not 256-byte aligned");
+    // shape checks first so that the workspace size below is meaningful
+    if (M < 1) return fail(FQ_ERR_SHAPE, fmt("%s: M=%d must be >= 1", fn, M));
+    FQ_TRY(check_k(fn, K));
+    FQ_TRY(check_bits(fn, "abits", abits));
+    const size_t need = fq_linear_workspace_bytes(M, K, abits);
+    if (workspace_bytes < need)
+        return fail(FQ_ERR_ARG, fmt("%s: workspace_bytes=%zu < %zu needed for M=%d K=%d abits=%d", fn,
+                                    workspace_bytes, need, M, K, abits));
+    uint8_t* codes = static_cast<uint8_t*>(workspace);
+    float* scales = reinterpret_cast<float*>(codes + round_up(code_bytes(M, K, abits), 256));
+    FQ_TRY(validate_prologue(fn, x_bf16, M, K, ldx, gamma_folded, eps, ascale, fold_after, hblock, abits, codes,
+                             scales));
+    FQ_TRY(validate_gemm(fn, codes, scales, M, abits, w_codes, wscale, N, K, wbits, bias, residual_bf16, ldr,
+                         y_bf16, ldy, true));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    fq::PrologueArgs a{static_cast<const uint16_t*>(x_bf16), M, K, ldx, gamma_folded, eps, ascale,
+                       fold_after, hblock, abits, codes, scales};
+    FQ_TRY(device_status(fn, fq::launch_prologue(a, s)));
+    fq::GemmArgs g{codes, scales, M, abits, static_cast<const uint8_t*>(w_codes), wscale, N, K, wbits, bias,
+                   static_cast<const uint16_t*>(residual_bf16), ldr, static_cast<uint16_t*>(y_bf16), ldy,
+                   nullptr};
+    return run_gemm(fn, g, s);
+}
+
+}  // extern "C"

@@ -1,0 +1,150 @@
+// Device helpers shared by the FoldQuant kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fq {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// Streaming loads that bypass cache allocation for data read exactly once.
+__device__ __forceinline__ uint4 load_stream16(const uint8_t* p) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ uint2 load_stream8(const uint8_t* p) {
+    const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+    return make_uint2(v[0], v[1]);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// float32 -> bfloat16 bits, round to nearest, ties to even (NaN -> quiet NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Operand fragments for v_mfma_i32_16x16x64_i8.  The MFMA sums over its 64 k
+// values in any order, so each operand only has to present the same k to the
+// same byte slot as the other operand.
+//
+// 8-bit codes: 16 bytes = k0..k15 in natural order.
+// 4-bit codes: 8 bytes = 16 nibbles (even k low).  Each nibble is moved into the
+// high half of a byte, which makes the byte exactly 16x the signed code:
+//   lo(d) = (d << 4) & 0xF0F0F0F0 -> 16*[k0, k2, k4, k6]
+//   hi(d) =  d       & 0xF0F0F0F0 -> 16*[k1, k3, k5, k7]
+// giving the k order [0,2,4,6, 1,3,5,7, 8,10,12,14, 9,11,13,15]; the product
+// is then 16x (one 4-bit side) or 256x (two) the true one and the
+// accumulator is shifted back exactly.  An 8-bit operand facing a 4-bit one is
+// byte-permuted into that same order.
+__device__ __forceinline__ v4i frag_from_nibbles(uint2 p) {
+    v4i r;
+    r[0] = int((p.x << 4) & 0xF0F0F0F0u);
+    r[1] = int(p.x & 0xF0F0F0F0u);
+    r[2] = int((p.y << 4) & 0xF0F0F0F0u);
+    r[3] = int(p.y & 0xF0F0F0F0u);
+    return r;
+}
+
+__device__ __forceinline__ v4i frag_from_bytes(uint4 p) {
+    v4i r;
+    r[0] = int(p.x);
+    r[1] = int(p.y);
+    r[2] = int(p.z);
+    r[3] = int(p.w);
+    return r;
+}
+
+// 16 natural-order bytes permuted into the nibble order above.
+__device__ __forceinline__ v4i frag_from_bytes_nibble_order(uint4 p) {
+    v4i r;
+    // __builtin_amdgcn_perm(hi, lo, sel): byte i of the result = byte sel_i of {hi:lo}
+    r[0] = int(__builtin_amdgcn_perm(p.y, p.x, 0x06040200u));  // k0 k2 k4 k6
+    r[1] = int(__builtin_amdgcn_perm(p.y, p.x, 0x07050301u));  // k1 k3 k5 k7
+    r[2] = int(__builtin_amdgcn_perm(p.w, p.z, 0x06040200u));  // k8 k10 k12 k14
+    r[3] = int(__builtin_amdgcn_perm(p.w, p.z, 0x07050301u));  // k9 k11 k13 k15
+    return r;
+}
+
+template <int BITS_SELF, int BITS_OTHER>
+struct Frag;
+
+template <>
+struct Frag<8, 8> {
+    static constexpr int kBytes = 16;
+    __device__ __forceinline__ static v4i load(const uint8_t* p) {
+        return frag_from_bytes(*reinterpret_cast<const uint4*>(p));
+    }
+};
+template <>
+struct Frag<8, 4> {
+    static constexpr int kBytes = 16;
+    __device__ __forceinline__ static v4i load(const uint8_t* p) {
+        return frag_from_bytes_nibble_order(*reinterpret_cast<const uint4*>(p));
+    }
+};
+template <int OTHER>
+struct Frag4 {
+    static constexpr int kBytes = 8;
+    __device__ __forceinline__ static v4i load(const uint8_t* p) {
+        return frag_from_nibbles(*reinterpret_cast<const uint2*>(p));
+    }
+};
+template <>
+struct Frag<4, 4> : Frag4<4> {};
+template <>
+struct Frag<4, 8> : Frag4<8> {};
+
+// Shift that undoes the 16x per 4-bit operand.
+template <int ABITS, int WBITS>
+struct AccShift {
+    static constexpr int value = (ABITS == 4 ? 4 : 0) + (WBITS == 4 ? 4 : 0);
+};
+
+__device__ __forceinline__ v4i mfma16x16x64(v4i a, v4i b, v4i c) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+// Epilogue for 4 consecutive output features n..n+3 of token m.
+__device__ __forceinline__ void store_out4(const v4i acc, int shift, int m, int n, float sa,
+                                           const float* __restrict__ wscale, const float* __restrict__ bias,
+                                           const uint16_t* __restrict__ residual, int64_t ldr,
+                                           uint16_t* __restrict__ y, int64_t ldy, int32_t* __restrict__ acc_out,
+                                           int N) {
+    const float4 sw = *reinterpret_cast<const float4*>(wscale + n);
+    int a0 = acc[0] >> shift, a1 = acc[1] >> shift, a2 = acc[2] >> shift, a3 = acc[3] >> shift;
+    float t0 = float(a0) * (sa * sw.x);
+    float t1 = float(a1) * (sa * sw.y);
+    float t2 = float(a2) * (sa * sw.z);
+    float t3 = float(a3) * (sa * sw.w);
+    if (bias) {
+        const float4 b = *reinterpret_cast<const float4*>(bias + n);
+        t0 = t0 + b.x;
+        t1 = t1 + b.y;
+        t2 = t2 + b.z;
+        t3 = t3 + b.w;
+    }
+    if (residual) {
+        const uint2 r = *reinterpret_cast<const uint2*>(residual + int64_t(m) * ldr + n);
+        t0 = t0 + bf16_lo(r.x);
+        t1 = t1 + bf16_hi(r.x);
+        t2 = t2 + bf16_lo(r.y);
+        t3 = t3 + bf16_hi(r.y);
+    }
+    uint2 o;
+    o.x = f32_to_bf16(t0) | (f32_to_bf16(t1) << 16);
+    o.y = f32_to_bf16(t2) | (f32_to_bf16(t3) << 16);
+    *reinterpret_cast<uint2*>(y + int64_t(m) * ldy + n) = o;
+    if (acc_out) {
+        int4 v = make_int4(a0, a1, a2, a3);
+        *reinterpret_cast<int4*>(acc_out + int64_t(m) * N + n) = v;
+    }
+}
+
+}  // namespace fq

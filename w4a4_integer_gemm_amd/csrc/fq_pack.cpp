@@ -1,0 +1,134 @@
+// Host-side weight packer: fold the smoothing vector and the block Hadamard
+// rotation into each weight row, then round it per row to symmetric INT8/INT4
+// codes with one float32 scale (vla.cpp FoldQuant page: INT8 or INT4 codes
+// with per-row scales in a block-Hadamard, SmoothQuant-folded frame; the
+// bring-up exporter does "rotation and per-row RTN").
+//
+// Fold algebra (dequant-mode commit of that page): the activation frame is
+// R(x/a) or R(x)/a, so for the product to stay x . w_n the stored row is
+// u_n = R(a . w_n) (fold before) or a . R(w_n) (fold after).  The fold runs in
+// float64; the butterfly runs its stages with span 1, 2, ..., b/2 and then
+// scales by 1/sqrt(b).  Codes round half-to-even against the stored float32
+// scale s_n = (float)(max|u_n| / qmax) and clamp to +-qmax.
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "../../include/fq.h"
+#include "fq_internal.h"
+
+namespace {
+
+void rotate_row(double* u, int32_t K, int32_t b) {
+    if (b > 1) {
+        for (int32_t base = 0; base < K; base += b) {
+            double* blk = u + base;
+            for (int32_t span = 1; span < b; span *= 2)
+                for (int32_t i0 = 0; i0 < b; i0 += 2 * span)
+                    for (int32_t i = i0; i < i0 + span; ++i) {
+                        const double lo = blk[i], hi = blk[i + span];
+                        blk[i] = lo + hi;
+                        blk[i + span] = lo - hi;
+                    }
+        }
+    }
+    const double norm = 1.0 / std::sqrt(static_cast<double>(b));
+    for (int32_t k = 0; k < K; ++k) u[k] *= norm;
+}
+
+void pack_rows(const float* W, int32_t n0, int32_t n1, int32_t K, const float* a, int32_t fold_after, int32_t b,
+               int32_t bits, uint8_t* codes, float* wscale) {
+    const int32_t qmax = bits == 8 ? 127 : 7;
+    const size_t row_bytes = bits == 8 ? size_t(K) : size_t(K / 2);
+    std::vector<double> u(K);
+    std::vector<int32_t> q(K);
+    for (int32_t n = n0; n < n1; ++n) {
+        const float* w = W + int64_t(n) * K;
+        for (int32_t k = 0; k < K; ++k) u[k] = static_cast<double>(w[k]);
+        if (a && !fold_after)
+            for (int32_t k = 0; k < K; ++k) u[k] *= static_cast<double>(a[k]);
+        rotate_row(u.data(), K, b);
+        if (a && fold_after)
+            for (int32_t k = 0; k < K; ++k) u[k] *= static_cast<double>(a[k]);
+        double amax = 0.0;
+        for (int32_t k = 0; k < K; ++k) amax = std::max(amax, std::fabs(u[k]));
+        const float s = static_cast<float>(amax / qmax);
+        const double sd = static_cast<double>(s);
+        for (int32_t k = 0; k < K; ++k) {
+            double r = s > 0.0f ? std::nearbyint(u[k] / sd) : 0.0;
+            r = std::min<double>(std::max<double>(r, -qmax), qmax);
+            q[k] = static_cast<int32_t>(r);
+        }
+        uint8_t* row = codes + size_t(n) * row_bytes;
+        if (bits == 8) {
+            for (int32_t k = 0; k < K; ++k) row[k] = static_cast<uint8_t>(static_cast<int8_t>(q[k]));
+        } else {
+            for (int32_t j = 0; j < K / 2; ++j)
+                row[j] = static_cast<uint8_t>((q[2 * j] & 0xF) | ((q[2 * j + 1] & 0xF) << 4));
+        }
+        wscale[n] = s;
+    }
+}
+
+}  // namespace
+
+extern "C" fq_status fq_pack_weights(const float* W, int32_t N, int32_t K, const float* ascale, int32_t fold_after,
+                                     int32_t hblock, int32_t wbits, void* codes_out, float* wscale_out) {
+    fq::clear_error();
+    auto fail = [](fq_status s, const std::string& m) {
+        fq::set_error(m);
+        return s;
+    };
+    if (!W || !codes_out || !wscale_out) return fail(FQ_ERR_ARG, "fq_pack_weights: W, codes_out or wscale_out is NULL");
+    char buf[256];
+    if (wbits != 8 && wbits != 4) {
+        snprintf(buf, sizeof buf, "fq_pack_weights: wbits=%d is not a supported code width (4 or 8)", wbits);
+        return fail(FQ_ERR_UNSUPPORTED, buf);
+    }
+    if (N < 1) {
+        snprintf(buf, sizeof buf, "fq_pack_weights: N=%d must be >= 1", N);
+        return fail(FQ_ERR_SHAPE, buf);
+    }
+    if (K < 64 || K > 65536 || K % 64) {
+        snprintf(buf, sizeof buf, "fq_pack_weights: K=%d must be a multiple of 64 in [64, 65536] (%d/64 = %.2f)", K,
+                 K, K / 64.0);
+        return fail(FQ_ERR_SHAPE, buf);
+    }
+    if (hblock < 1 || hblock > 256 || (hblock & (hblock - 1))) {
+        snprintf(buf, sizeof buf, "fq_pack_weights: hblock=%d must be a power of two in [1, 256]", hblock);
+        return fail(FQ_ERR_SHAPE, buf);
+    }
+    if (K % hblock) {
+        snprintf(buf, sizeof buf, "fq_pack_weights: K=%d not divisible by hblock=%d (%d/%d = %.2f)", K, hblock, K,
+                 hblock, double(K) / hblock);
+        return fail(FQ_ERR_SHAPE, buf);
+    }
+    if (fold_after != 0 && fold_after != 1) {
+        snprintf(buf, sizeof buf, "fq_pack_weights: fold_after=%d must be 0 or 1", fold_after);
+        return fail(FQ_ERR_ARG, buf);
+    }
+    if (ascale)
+        for (int32_t k = 0; k < K; ++k)
+            if (!(ascale[k] > 0.0f) || !std::isfinite(ascale[k])) {
+                snprintf(buf, sizeof buf, "fq_pack_weights: ascale[%d]=%g must be finite and > 0", k,
+                         double(ascale[k]));
+                return fail(FQ_ERR_ARG, buf);
+            }
+    unsigned nt = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
+    nt = std::min<unsigned>(nt, unsigned(N));
+    std::vector<std::thread> pool;
+    const int32_t per = (N + int32_t(nt) - 1) / int32_t(nt);
+    for (unsigned t = 0; t < nt; ++t) {
+        const int32_t n0 = int32_t(t) * per, n1 = std::min(N, n0 + per);
+        if (n0 >= n1) break;
+        pool.emplace_back(pack_rows, W, n0, n1, K, ascale, fold_after, hblock, wbits,
+                          static_cast<uint8_t*>(codes_out), wscale_out);
+    }
+    for (auto& th : pool) th.join();
+    return FQ_OK;
+}
