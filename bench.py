@@ -151,7 +151,7 @@ def bench_decode(name, steps, warmup, copies=5):
                 gemv_gbs=gemv_bytes / (ms_gemv * 1e-3) / 1e9, bytes=nbytes, gemv_bytes=gemv_bytes)
 
 
-def cpu_baseline(name, min_seconds=10.0, max_reps=40):
+def cpu_baseline(name, min_seconds=10.0, max_reps=400):
     """The oracle (plain C + OpenMP) on the same workload, repeated until about
     min_seconds of CPU work: whole fq_linear (prologue, integer GEMM, epilogue)."""
     import oracle

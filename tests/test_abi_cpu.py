@@ -92,7 +92,8 @@ def test_fold_gain_matches_oracle():
 @pytest.mark.parametrize("kw,match", [
     (dict(wbits=3), "wbits=3"),
     (dict(K=100), "K=100"),
-    (dict(K=192, hblock=128), r"K=192 not divisible by hblock=128 \(192/128 = 1.50\)"),
+    (dict(K=192), r"K=192 must be a multiple of 128"),
+    (dict(K=384, hblock=256), r"K=384 not divisible by hblock=256 \(384/256 = 1.50\)"),
     (dict(hblock=3), "hblock=3"),
     (dict(hblock=512), "hblock=512"),
     (dict(fold_after=2), "fold_after=2"),
@@ -119,7 +120,7 @@ def _prologue(**kw):
     (dict(codes=None), 1, "act_codes is NULL"),
     (dict(scale=None), 1, "act_scale is NULL"),
     (dict(M=0), 2, "M=0"),
-    (dict(K=96, ldx=96), 2, r"K=96 is not a multiple of the MFMA depth 64 \(96/64 = 1.50\)"),
+    (dict(K=100, ldx=104), 2, r"K=100 is not a multiple of 8 \(100/8 = 12.50\)"),
     (dict(K=131072, ldx=131072), 2, "K=131072 outside"),
     (dict(hblock=48), 2, "hblock=48"),
     (dict(K=320, ldx=320, hblock=128), 2, r"K=320 not divisible by hblock=128 \(320/128 = 2.50\)"),
@@ -159,6 +160,7 @@ def _gemm(**kw):
     (dict(w=BAD), 4, "w_codes is not 16-byte aligned"),
     (dict(acc=BAD), 4, "acc_i32 is not 16-byte aligned"),
     (dict(K=0), 2, "K=0"),
+    (dict(K=192), 2, r"K=192 is not a multiple of 128 \(192/128 = 1.50\)"),
 ])
 def test_gemm_rejects_before_device_work(kw, status, match):
     rc = _gemm(**kw)
@@ -195,7 +197,7 @@ def test_linear_rejects_before_device_work(kw, status, match):
 def test_error_message_is_cleared_by_a_good_host_call():
     _gemm(N=0)
     assert fq.last_error()
-    fq.fq_pack_weights(np.ones((2, 64), np.float32), None, 0, 64, 8)
+    fq.fq_pack_weights(np.ones((2, 128), np.float32), None, 0, 64, 8)
     assert fq.last_error() == ""
 
 

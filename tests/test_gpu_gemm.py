@@ -49,10 +49,12 @@ def run_gemm(M, N, K, abits, wbits, seed, bias=False, residual=False, extreme=Fa
 
 SHAPES = [
     # M, N, K  (M <= 32 takes the GEMV kernel)
-    (1, 8, 64), (1, 520, 3584), (5, 136, 192), (16, 512, 256), (17, 264, 640), (32, 1000, 1024),
-    (33, 8, 64), (33, 136, 192), (64, 128, 128), (100, 392, 704), (128, 256, 3584), (130, 520, 256),
+    (1, 8, 128), (1, 520, 3584), (5, 136, 384), (16, 512, 256), (17, 264, 768), (32, 1000, 1024),
+    (33, 8, 128), (33, 136, 384), (64, 128, 128), (100, 392, 768), (128, 256, 3584), (130, 520, 256),
     (300, 1000, 2048), (816, 264, 1024),
 ]
+
+TILES = ["128x128", "128x144", "128x112", "256x128", "128x256", "64x128"]
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "M{}_N{}_K{}".format(*s))
@@ -83,3 +85,17 @@ def test_gemm_strided_output_and_residual():
         acc, acc_ref, yg, yf, sa, sw, b, res = run_gemm(M, 136, 256, 8, 8, seed=9, residual=True, ldy=144, ldr=152)
         assert np.array_equal(acc, acc_ref)
         assert_y_elementwise(yg, yf, acc_ref, sa, sw, None, res, what=f"strided M={M}")
+
+
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("bits", [(8, 8), (4, 4), (8, 4), (4, 8)], ids=lambda b: "A{}W{}".format(*b))
+def test_gemm_every_tile_shape(tile, bits, monkeypatch):
+    """Each tile shape of the MFMA kernel (forced through the FQ_GEMM_TILE test hook)
+    on a ragged problem: M and N not multiples of the tile, several k stages."""
+    monkeypatch.setenv("FQ_GEMM_TILE", tile)
+    log(f"gemm tile {tile} bits {bits}")
+    for M, N, K in ((300, 392, 768), (33, 1000, 1280)):
+        acc, acc_ref, yg, yf, sa, sw, b, res = run_gemm(M, N, K, bits[0], bits[1], seed=M + N, bias=True,
+                                                        residual=True)
+        assert np.array_equal(acc, acc_ref), f"{tile}: {np.count_nonzero(acc != acc_ref)} accumulators differ"
+        assert_y_elementwise(yg, yf, acc_ref, sa, sw, b, res, what=f"{tile} M{M} N{N} K{K}")

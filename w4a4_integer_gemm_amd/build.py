@@ -2,7 +2,7 @@
 
 Every object is compiled for gfx950 only, with IEEE float32 divide and sqrt,
 no floating-point contraction (the exactness rules of the vla.cpp FoldQuant
-page) and packed-FP32 instructions disabled."""
+page), packed-FP32 instructions disabled and MFMA accumulators in VGPRs."""
 import os
 import subprocess
 import sys
@@ -22,6 +22,9 @@ CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
     "-fhip-fp32-correctly-rounded-divide-sqrt", "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA accumulators in ordinary VGPRs: the mixed AGPR/VGPR assignment
+    # the default heuristic picks shuffles accumulators between the two files
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
 

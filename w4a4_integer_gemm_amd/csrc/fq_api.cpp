@@ -42,6 +42,8 @@ bool is_pow2(int64_t v) { return v >= 1 && (v & (v - 1)) == 0; }
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 constexpr int32_t kMaxK = 65536;
+constexpr int32_t kProloguePack = 8;   // one 16-byte bf16 load per lane
+constexpr int32_t kGemmK = 128;        // one k stage of the GEMM
 
 // Checks shared by the prologue, the GEMM and the packer.  Returns FQ_OK or the failure.
 fq_status check_bits(const char* fn, const char* name, int32_t bits) {
@@ -50,12 +52,14 @@ fq_status check_bits(const char* fn, const char* name, int32_t bits) {
     return FQ_OK;
 }
 
-fq_status check_k(const char* fn, int32_t K) {
-    if (K < 64 || K > kMaxK)
-        return fail(FQ_ERR_SHAPE, fmt("%s: K=%d outside [64, %d]", fn, K, kMaxK));
-    if (K % 64)
-        return fail(FQ_ERR_SHAPE, fmt("%s: K=%d is not a multiple of the MFMA depth 64 (%d/64 = %.2f)",
-                                      fn, K, K, K / 64.0));
+// K bounds; `mult` is the granularity the entry point needs (8 for the
+// prologue's 16-byte lanes, 128 for the GEMM's k stages).
+fq_status check_k(const char* fn, int32_t K, int32_t mult) {
+    if (K < mult || K > kMaxK)
+        return fail(FQ_ERR_SHAPE, fmt("%s: K=%d outside [%d, %d]", fn, K, mult, kMaxK));
+    if (K % mult)
+        return fail(FQ_ERR_SHAPE, fmt("%s: K=%d is not a multiple of %d (%d/%d = %.2f)", fn, K, mult, K, mult,
+                                      double(K) / mult));
     return FQ_OK;
 }
 
@@ -81,7 +85,7 @@ fq_status validate_prologue(const char* fn, const void* x, int32_t M, int32_t K,
     if (!codes) return fail(FQ_ERR_ARG, fmt("%s: act_codes is NULL", fn));
     if (!scale) return fail(FQ_ERR_ARG, fmt("%s: act_scale is NULL", fn));
     if (M < 1) return fail(FQ_ERR_SHAPE, fmt("%s: M=%d must be >= 1", fn, M));
-    FQ_TRY(check_k(fn, K));
+    FQ_TRY(check_k(fn, K, kProloguePack));
     FQ_TRY(check_bits(fn, "abits", abits));
     FQ_TRY(check_hblock(fn, K, hblock));
     if (ldx < K) return fail(FQ_ERR_SHAPE, fmt("%s: ldx=%lld < K=%d", fn, (long long)ldx, K));
@@ -110,7 +114,7 @@ fq_status validate_gemm(const char* fn, const void* act, const float* act_scale,
     if (M < 1) return fail(FQ_ERR_SHAPE, fmt("%s: M=%d must be >= 1", fn, M));
     if (N < 1) return fail(FQ_ERR_SHAPE, fmt("%s: N=%d must be >= 1", fn, N));
     if (N % 8) return fail(FQ_ERR_SHAPE, fmt("%s: N=%d is not a multiple of 8 (%d/8 = %.3f)", fn, N, N, N / 8.0));
-    FQ_TRY(check_k(fn, K));
+    FQ_TRY(check_k(fn, K, kGemmK));
     FQ_TRY(check_bits(fn, "abits", abits));
     FQ_TRY(check_bits(fn, "wbits", wbits));
     if (ldy < N) return fail(FQ_ERR_SHAPE, fmt("%s: ldy=%lld < N=%d", fn, (long long)ldy, N));
@@ -214,7 +218,7 @@ fq_status fq_linear(const void* x_bf16, int32_t M, int32_t K, int64_t ldx, const
     if (!aligned(workspace, 256)) return fail(FQ_ERR_ALIGN, "fq_linear: workspace is not 256-byte aligned");
     // shape checks first so that the workspace size below is meaningful
     if (M < 1) return fail(FQ_ERR_SHAPE, fmt("%s: M=%d must be >= 1", fn, M));
-    FQ_TRY(check_k(fn, K));
+    FQ_TRY(check_k(fn, K, kGemmK));
     FQ_TRY(check_bits(fn, "abits", abits));
     const size_t need = fq_linear_workspace_bytes(M, K, abits);
     if (workspace_bytes < need)

@@ -94,9 +94,9 @@ extern "C" fq_status fq_pack_weights(const float* W, int32_t N, int32_t K, const
         snprintf(buf, sizeof buf, "fq_pack_weights: N=%d must be >= 1", N);
         return fail(FQ_ERR_SHAPE, buf);
     }
-    if (K < 64 || K > 65536 || K % 64) {
-        snprintf(buf, sizeof buf, "fq_pack_weights: K=%d must be a multiple of 64 in [64, 65536] (%d/64 = %.2f)", K,
-                 K, K / 64.0);
+    if (K < 128 || K > 65536 || K % 128) {
+        snprintf(buf, sizeof buf, "fq_pack_weights: K=%d must be a multiple of 128 in [128, 65536] (%d/128 = %.2f)",
+                 K, K, K / 128.0);
         return fail(FQ_ERR_SHAPE, buf);
     }
     if (hblock < 1 || hblock > 256 || (hblock & (hblock - 1))) {
