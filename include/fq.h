@@ -37,7 +37,8 @@
  *     than the error message.  Inputs are read only; outputs are overwritten.
  *   - Device entry points are asynchronous on `stream` (a hipStream_t passed as
  *     void*; NULL is the null stream) and take device pointers.
- *   - Shapes: M, N >= 1; K a multiple of 64 (the MFMA depth), 64 <= K <= 65536;
+ *   - Shapes: M, N >= 1; N a multiple of 8; K <= 65536, a multiple of 32 for
+ *     fq_prologue and of 128 for fq_pack_weights, fq_gemm and fq_linear;
  *     hblock a power of two in [1, 256] dividing K (1 = no rotation); bits in
  *     {4, 8} for both weights and activations (W8A8, W4A4, W4A8, W8A4).
  *   - Alignment: bf16 rows (x, residual, y) need a 16-byte aligned base and a

@@ -120,8 +120,9 @@ def _prologue(**kw):
     (dict(codes=None), 1, "act_codes is NULL"),
     (dict(scale=None), 1, "act_scale is NULL"),
     (dict(M=0), 2, "M=0"),
-    (dict(K=100, ldx=104), 2, r"K=100 is not a multiple of 8 \(100/8 = 12.50\)"),
+    (dict(K=100, ldx=104), 2, r"K=100 is not a multiple of 32 \(100/32 = 3.12\)"),
     (dict(K=131072, ldx=131072), 2, "K=131072 outside"),
+    (dict(K=40992, ldx=40992, hblock=32), 2, r"K=40992 above 32768 must be a multiple of 64"),
     (dict(hblock=48), 2, "hblock=48"),
     (dict(K=320, ldx=320, hblock=128), 2, r"K=320 not divisible by hblock=128 \(320/128 = 2.50\)"),
     (dict(abits=2), 3, "abits=2"),

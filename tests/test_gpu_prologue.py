@@ -28,11 +28,13 @@ CASES = [
     (64, 3584, 128, 8, True, "gain", 0),
     (8, 3584, 128, 4, False, "explicit", 1),
     (4, 8192, 128, 8, True, "none", 0),
-    (3, 8256, 64, 8, True, "gain", 0),      # 1032 lanes -> two passes, ragged
+    (3, 8256, 64, 8, True, "gain", 0),      # 64 values per lane, 129 lanes
+    (3, 8224, 32, 4, True, "none", 0),      # K % 64 = 32 -> 32 values per lane, 257 lanes
+    (2, 32768, 256, 8, False, "explicit", 1),
     (6, 16384, 128, 4, False, "none", 0),
     (5, 18944, 128, 8, False, "none", 0),
     (2, 18944, 256, 4, True, "explicit", 0),
-    (2, 65536, 128, 8, True, "gain", 0),    # the largest K the ABI takes (8 passes)
+    (2, 65536, 128, 8, True, "gain", 0),    # the largest K the ABI takes (1024 lanes of 64)
 ]
 
 

@@ -42,7 +42,7 @@ bool is_pow2(int64_t v) { return v >= 1 && (v & (v - 1)) == 0; }
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 constexpr int32_t kMaxK = 65536;
-constexpr int32_t kProloguePack = 8;   // one 16-byte bf16 load per lane
+constexpr int32_t kProloguePack = 32;  // 32 bf16 values per prologue lane
 constexpr int32_t kGemmK = 128;        // one k stage of the GEMM
 
 // Checks shared by the prologue, the GEMM and the packer.  Returns FQ_OK or the failure.
@@ -53,7 +53,7 @@ fq_status check_bits(const char* fn, const char* name, int32_t bits) {
 }
 
 // K bounds; `mult` is the granularity the entry point needs (8 for the
-// prologue's 16-byte lanes, 128 for the GEMM's k stages).
+// prologue's 32-value lanes, 128 for the GEMM's k stages).
 fq_status check_k(const char* fn, int32_t K, int32_t mult) {
     if (K < mult || K > kMaxK)
         return fail(FQ_ERR_SHAPE, fmt("%s: K=%d outside [%d, %d]", fn, K, mult, kMaxK));
@@ -86,6 +86,9 @@ fq_status validate_prologue(const char* fn, const void* x, int32_t M, int32_t K,
     if (!scale) return fail(FQ_ERR_ARG, fmt("%s: act_scale is NULL", fn));
     if (M < 1) return fail(FQ_ERR_SHAPE, fmt("%s: M=%d must be >= 1", fn, M));
     FQ_TRY(check_k(fn, K, kProloguePack));
+    if (K > 32768 && K % 64)
+        return fail(FQ_ERR_SHAPE, fmt("%s: K=%d above 32768 must be a multiple of 64 (%d/64 = %.2f)", fn, K, K,
+                                      K / 64.0));
     FQ_TRY(check_bits(fn, "abits", abits));
     FQ_TRY(check_hblock(fn, K, hblock));
     if (ldx < K) return fail(FQ_ERR_SHAPE, fmt("%s: ldx=%lld < K=%d", fn, (long long)ldx, K));

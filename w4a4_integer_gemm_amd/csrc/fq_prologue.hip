@@ -3,16 +3,26 @@
 // RMSNorm with the folded gain, the ascale divide, the block rotation, a
 // per-token amax scale, round-half-even and a clamp).
 //
-// Layout: one workgroup per token.  Lane t of the workgroup owns 8 consecutive
-// bf16 values (one 16-byte load) per pass; a token of K values takes K/8 lanes
-// spread over P passes (P <= 8, so K <= 65536).  A Hadamard block of b values is
-// b/8 consecutive lanes of one wavefront (b <= 256 -> at most 32 lanes), so
-// the butterfly's first three stages (span 1, 2, 4) run inside a lane's
-// registers and the later ones (span 8 .. b/2) exchange across lanes.  Every
-// element goes through the same float32 operations in the same order as the
-// definition (stage spans 1, 2, 4, ...), so the rotation is bit-reproducible.
-// The whole token stays in registers between the two reductions (sum of
-// squares, then amax), so x is read from HBM once and the codes written once.
+// Layout: one workgroup per token.  Lane t owns E = 32 (K <= 32768) or 64
+// consecutive bf16 values (E/8 16-byte loads), so a token of up to 65536 values
+// is one pass of at most 1024 lanes.  The butterfly's first log2(E) stages
+// (span 1 .. E/2) run inside a lane's registers; a Hadamard block of b > E
+// values spans b/E consecutive lanes, whose stages (span E .. b/2) exchange
+// values with DPP lane permutations (xor 1, xor 2, and xor 4 composed from two
+// permutations) and one fused multiply-add per value.  Every element goes
+// through the same float32 operations in the same order as the definition
+// (stage spans 1, 2, 4, ...), so the rotation is bit-reproducible.  The token
+// stays in registers between the two reductions (sum of squares, amax): x is
+// read from HBM once and the codes written once.
+//
+// Quantisation divides by the per-token scale s.  The quotient is computed as
+// q0 = h * r, rem = fma(-s, q0, h), q = fma(rem, r, q0) with r = 1/s (one IEEE
+// divide per token): with r correctly rounded and no underflow in the
+// remainder this is the correctly rounded h / s (Markstein's theorem), so it
+// equals the IEEE quotient bit for bit.  The fast form is used when
+// 2^-100 <= s <= 2^100 (r stays normal and the remainder cannot underflow for
+// any |h| whose quotient could round away from zero); other scales divide per
+// element.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -26,219 +36,338 @@ namespace {
 constexpr int kMaxThreads = 1024;
 constexpr int kMaxWaves = kMaxThreads / 64;
 
-template <typename T>
-__device__ __forceinline__ T wave_sum(T v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-    return v;
+// Whole-wave reductions on the VALU: DPP within rows of 16 lanes (xor 1,
+// xor 2, half-row mirror, row mirror), then the gfx950 row swaps (lanes
+// l <-> l ^ 16 and l <-> l ^ 32).  Each step combines two complete partial
+// results, so every lane ends with the same value, in a fixed order.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
 }
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    v = fmaxf(v, __int_as_float(dpp_i<0xB1>(__float_as_int(v))));   // quad_perm [1,0,3,2]
+    v = fmaxf(v, __int_as_float(dpp_i<0x4E>(__float_as_int(v))));   // quad_perm [2,3,0,1]
+    v = fmaxf(v, __int_as_float(dpp_i<0x141>(__float_as_int(v))));  // row_half_mirror
+    v = fmaxf(v, __int_as_float(dpp_i<0x140>(__float_as_int(v))));  // row_mirror
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
+    v = fmaxf(__int_as_float(a[0]), __int_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+    return fmaxf(__int_as_float(b[0]), __int_as_float(b[1]));
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+    const long long u = __double_as_longlong(v);
+    const int lo = dpp_i<CTRL>(int(u)), hi = dpp_i<CTRL>(int(u >> 32));
+    return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned int>(lo));
+}
+
+__device__ __forceinline__ double join_d(int lo, int hi) {
+    return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned int>(lo));
+}
+
+__device__ __forceinline__ double wave_sum(double v) {
+    v = v + dpp_d<0xB1>(v);
+    v = v + dpp_d<0x4E>(v);
+    v = v + dpp_d<0x141>(v);
+    v = v + dpp_d<0x140>(v);
+    {
+        const long long u = __double_as_longlong(v);
+        const auto lo = __builtin_amdgcn_permlane16_swap(int(u), int(u), false, false);
+        const auto hi = __builtin_amdgcn_permlane16_swap(int(u >> 32), int(u >> 32), false, false);
+        v = join_d(lo[0], hi[0]) + join_d(lo[1], hi[1]);
+    }
+    {
+        const long long u = __double_as_longlong(v);
+        const auto lo = __builtin_amdgcn_permlane32_swap(int(u), int(u), false, false);
+        const auto hi = __builtin_amdgcn_permlane32_swap(int(u >> 32), int(u >> 32), false, false);
+        v = join_d(lo[0], hi[0]) + join_d(lo[1], hi[1]);
+    }
     return v;
 }
 
-template <int P, int ABITS>
-__global__ __launch_bounds__(kMaxThreads) void prologue_kernel(
-    const uint16_t* __restrict__ x, int K, int64_t ldx, const float* __restrict__ gamma, float eps,
-    const float* __restrict__ ascale, int fold_after, int hblock, float rs, uint8_t* __restrict__ codes,
-    float* __restrict__ act_scale) {
+// value held by lane (lane ^ d) of the same wave, d in {1, 2, 4}, via DPP
+template <int D>
+__device__ __forceinline__ float lane_xor(float v) {
+    const int i = __float_as_int(v);
+    if (D == 1) return __int_as_float(__builtin_amdgcn_mov_dpp(i, 0xB1, 0xF, 0xF, true));  // quad_perm [1,0,3,2]
+    if (D == 2) return __int_as_float(__builtin_amdgcn_mov_dpp(i, 0x4E, 0xF, 0xF, true));  // quad_perm [2,3,0,1]
+    // xor 4 = (xor 7 within 8 lanes: row_half_mirror) then (xor 3: quad_perm [3,2,1,0])
+    const int m = __builtin_amdgcn_mov_dpp(i, 0x141, 0xF, 0xF, true);
+    return __int_as_float(__builtin_amdgcn_mov_dpp(m, 0x1B, 0xF, 0xF, true));
+}
+
+// one cross-lane butterfly stage: the lower lane of each pair keeps lo + hi,
+// the upper lane lo - hi (sign * v is exact, so the fma rounds exactly once)
+template <int D, int E>
+__device__ __forceinline__ void cross_stage(float (&v)[E], int lane) {
+    const float sgn = (lane & D) ? -1.0f : 1.0f;
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[i] = __builtin_fmaf(sgn, v[i], lane_xor<D>(v[i]));
+}
+
+__device__ __forceinline__ void unpack8(uint4 d, float* o) {
+    o[0] = bf16_lo(d.x);
+    o[1] = bf16_hi(d.x);
+    o[2] = bf16_lo(d.y);
+    o[3] = bf16_hi(d.y);
+    o[4] = bf16_lo(d.z);
+    o[5] = bf16_hi(d.z);
+    o[6] = bf16_lo(d.w);
+    o[7] = bf16_hi(d.w);
+}
+
+template <int E>
+__device__ __forceinline__ void divide_by_vector(float (&v)[E], const float* __restrict__ a, int c, bool active) {
+    if (active) {
+#pragma unroll
+        for (int q = 0; q < E / 4; ++q) {
+            const float4 d = *reinterpret_cast<const float4*>(a + E * c + 4 * q);
+            v[4 * q + 0] = v[4 * q + 0] / d.x;
+            v[4 * q + 1] = v[4 * q + 1] / d.y;
+            v[4 * q + 2] = v[4 * q + 2] / d.z;
+            v[4 * q + 3] = v[4 * q + 3] / d.w;
+        }
+    }
+}
+
+// One workgroup per token; lane t owns values [E t, E t + E) of the token.
+// PREG: the RMSNorm gain is loaded together with x (registers permitting).
+// Sum / max of a lane's E values as a balanced tree (short dependency chain).
+template <int E>
+__device__ __forceinline__ double lane_sumsq(const float (&v)[E]) {
+    // x*x is exact in float64, so fma(x, x, t) rounds exactly like x*x + t
+    double t[E / 2];
+#pragma unroll
+    for (int i = 0; i < E / 2; ++i) {
+        const double a = double(v[2 * i]), b = double(v[2 * i + 1]);
+        t[i] = __builtin_fma(b, b, a * a);
+    }
+#pragma unroll
+    for (int w = E / 4; w >= 1; w >>= 1)
+#pragma unroll
+        for (int i = 0; i < w; ++i) t[i] = t[i] + t[i + w];
+    return t[0];
+}
+
+template <int E>
+__device__ __forceinline__ float lane_absmax(const float (&v)[E]) {
+    float t[E / 2];
+#pragma unroll
+    for (int i = 0; i < E / 2; ++i) t[i] = fmaxf(fabsf(v[2 * i]), fabsf(v[2 * i + 1]));
+#pragma unroll
+    for (int w = E / 4; w >= 1; w >>= 1)
+#pragma unroll
+        for (int i = 0; i < w; ++i) t[i] = fmaxf(t[i], t[i + w]);
+    return t[0];
+}
+
+// Adding 1.5 * 2^23 to |q| <= 2^22 rounds q to an integer, ties to even (the
+// add itself rounds to nearest even at unit spacing), and leaves that integer
+// in the low mantissa bits: the low byte of the sum is the two's complement code.
+__device__ __forceinline__ uint32_t round_to_code_bits(float q) { return __float_as_uint(q + 0x1.8p23f); }
+
+// One workgroup per token; lane t owns values [E t, E t + E) of the token.
+// NORM: RMSNorm with the gain (loaded together with x); AMODE: explicit
+// smoothing divide 0 none, 1 before the rotation, 2 after it; the Hadamard
+// block is 2^LOG2B (compile time, so skipped stages cost no code).
+template <int E, int ABITS, bool NORM, int AMODE, int LOG2B>
+__global__ __launch_bounds__(kMaxThreads) void prologue_kernel(const uint16_t* __restrict__ x, int K, int64_t ldx,
+                                                                const float* __restrict__ gamma, float eps,
+                                                                const float* __restrict__ ascale, float rs,
+                                                                uint8_t* __restrict__ codes,
+                                                                float* __restrict__ act_scale) {
+    constexpr int hblock = 1 << LOG2B;
     constexpr int qmax = ABITS == 8 ? 127 : 7;
     __shared__ double red_d[kMaxWaves];
     __shared__ float red_f[kMaxWaves];
 
     const int m = blockIdx.x;
     const int T = blockDim.x;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int c = threadIdx.x;
+    const int lane = c & 63;
+    const int wave = c >> 6;
     const int nwaves = T >> 6;
-    const int nchunks = K >> 3;
+    const bool active = c < K / E;  // lanes past K hold zeros and only join the exchanges
     const uint16_t* xr = x + int64_t(m) * ldx;
 
-    float v[P][8];
+    constexpr bool kPreG = NORM && E <= 32;  // the gain comes with x while registers allow
+    float v[E];
+    float4 g[kPreG ? E / 4 : 1];
+    {
+        uint4 d[E / 8];
 #pragma unroll
-    for (int p = 0; p < P; ++p) {
-        const int c = p * T + tid;
-        uint4 d = make_uint4(0, 0, 0, 0);
-        if (c < nchunks) d = *reinterpret_cast<const uint4*>(xr + 8 * c);
-        v[p][0] = bf16_lo(d.x);
-        v[p][1] = bf16_hi(d.x);
-        v[p][2] = bf16_lo(d.y);
-        v[p][3] = bf16_hi(d.y);
-        v[p][4] = bf16_lo(d.z);
-        v[p][5] = bf16_hi(d.z);
-        v[p][6] = bf16_lo(d.w);
-        v[p][7] = bf16_hi(d.w);
+        for (int q = 0; q < E / 8; ++q) d[q] = make_uint4(0, 0, 0, 0);
+        if (active) {
+#pragma unroll
+            for (int q = 0; q < E / 8; ++q) d[q] = *reinterpret_cast<const uint4*>(xr + E * c + 8 * q);
+            if (kPreG) {
+#pragma unroll
+                for (int q = 0; q < E / 4; ++q) g[q] = *reinterpret_cast<const float4*>(gamma + E * c + 4 * q);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < E / 8; ++q) unpack8(d[q], &v[8 * q]);
     }
 
     // RMSNorm with the folded gain: the float32 squares are exact in float64
-    if (gamma) {
-        double ss = 0.0;
-#pragma unroll
-        for (int p = 0; p < P; ++p)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) ss += double(v[p][i]) * double(v[p][i]);
-        ss = wave_sum(ss);
-        if (lane == 0) red_d[wave] = ss;
-        __syncthreads();
-        double tot = 0.0;
-        for (int w = 0; w < nwaves; ++w) tot += red_d[w];
-        const float ms = float(tot / double(K));
+    if (NORM) {
+        double ss = wave_sum(lane_sumsq<E>(v));
+        if (nwaves > 1) {
+            if (lane == 0) red_d[wave] = ss;
+            __syncthreads();
+            ss = 0.0;
+            for (int w = 0; w < nwaves; ++w) ss += red_d[w];
+        }
+        const float ms = float(ss / double(K));
         const float rinv = 1.0f / sqrtf(ms + eps);
+        if (active) {
 #pragma unroll
-        for (int p = 0; p < P; ++p) {
-            const int c = p * T + tid;
-            if (c < nchunks) {
-                const float4 g0 = *reinterpret_cast<const float4*>(gamma + 8 * c);
-                const float4 g1 = *reinterpret_cast<const float4*>(gamma + 8 * c + 4);
-                const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-#pragma unroll
-                for (int i = 0; i < 8; ++i) v[p][i] = (v[p][i] * rinv) * g[i];
+            for (int q = 0; q < E / 4; ++q) {
+                const float4 gq = kPreG ? g[q < (kPreG ? E / 4 : 1) ? q : 0]
+                                        : *reinterpret_cast<const float4*>(gamma + E * c + 4 * q);
+                v[4 * q + 0] = (v[4 * q + 0] * rinv) * gq.x;
+                v[4 * q + 1] = (v[4 * q + 1] * rinv) * gq.y;
+                v[4 * q + 2] = (v[4 * q + 2] * rinv) * gq.z;
+                v[4 * q + 3] = (v[4 * q + 3] * rinv) * gq.w;
             }
         }
     }
 
-    // explicit smoothing divide before the rotation
-    if (ascale && !fold_after) {
-#pragma unroll
-        for (int p = 0; p < P; ++p) {
-            const int c = p * T + tid;
-            if (c < nchunks) {
-                const float4 a0 = *reinterpret_cast<const float4*>(ascale + 8 * c);
-                const float4 a1 = *reinterpret_cast<const float4*>(ascale + 8 * c + 4);
-                const float a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-#pragma unroll
-                for (int i = 0; i < 8; ++i) v[p][i] = v[p][i] / a[i];
-            }
-        }
-    }
+    if (AMODE == 1) divide_by_vector<E>(v, ascale, c, active);
 
-    // block Hadamard butterfly: spans 1, 2, 4 inside the lane ...
+    // block Hadamard butterfly: spans 1 .. E/2 inside the lane ...
 #pragma unroll
-    for (int span = 1; span < 8; span <<= 1) {
-        if (span < hblock) {
+    for (int span = 1; span < E; span <<= 1) {
+        if (span < hblock) {  // compile-time
 #pragma unroll
-            for (int p = 0; p < P; ++p)
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    if ((i & span) == 0) {
-                        const float lo = v[p][i], hi = v[p][i + span];
-                        v[p][i] = lo + hi;
-                        v[p][i + span] = lo - hi;
-                    }
+            for (int i = 0; i < E; ++i)
+                if ((i & span) == 0) {
+                    const float lo = v[i], hi = v[i + span];
+                    v[i] = lo + hi;
+                    v[i + span] = lo - hi;
+                }
         }
     }
-    // ... spans 8 .. b/2 across lanes (lane distance span/8)
-    for (int d = 1; 8 * d < hblock; d <<= 1) {
-        const bool upper = (lane & d) != 0;
+    // ... spans E .. b/2 across lanes (lane distance span / E)
+    if constexpr (hblock > E) cross_stage<1, E>(v, lane);
+    if constexpr (hblock > 2 * E) cross_stage<2, E>(v, lane);
+    if constexpr (hblock > 4 * E) cross_stage<4, E>(v, lane);
 #pragma unroll
-        for (int p = 0; p < P; ++p)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float other = __shfl_xor(v[p][i], d);
-                // lower lane holds the first operand: lo + hi; upper lane: lo - hi
-                v[p][i] = upper ? (other - v[p][i]) : (v[p][i] + other);
-            }
-    }
-#pragma unroll
-    for (int p = 0; p < P; ++p)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[p][i] = v[p][i] * rs;
+    for (int i = 0; i < E; ++i) v[i] = v[i] * rs;
 
-    // explicit smoothing divide after the rotation
-    if (ascale && fold_after) {
-#pragma unroll
-        for (int p = 0; p < P; ++p) {
-            const int c = p * T + tid;
-            if (c < nchunks) {
-                const float4 a0 = *reinterpret_cast<const float4*>(ascale + 8 * c);
-                const float4 a1 = *reinterpret_cast<const float4*>(ascale + 8 * c + 4);
-                const float a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-#pragma unroll
-                for (int i = 0; i < 8; ++i) v[p][i] = v[p][i] / a[i];
-            }
-        }
-    }
+    if (AMODE == 2) divide_by_vector<E>(v, ascale, c, active);
 
     // per-token amax (lanes past K hold zeros)
-    float amax = 0.0f;
-#pragma unroll
-    for (int p = 0; p < P; ++p)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[p][i]));
-    amax = wave_max(amax);
-    if (lane == 0) red_f[wave] = amax;
-    __syncthreads();
-    amax = 0.0f;
-    for (int w = 0; w < nwaves; ++w) amax = fmaxf(amax, red_f[w]);
+    float amax = wave_max(lane_absmax<E>(v));
+    if (nwaves > 1) {
+        if (lane == 0) red_f[wave] = amax;
+        __syncthreads();
+        amax = 0.0f;
+        for (int w = 0; w < nwaves; ++w) amax = fmaxf(amax, red_f[w]);
+    }
     const float s = amax / float(qmax);
+    const bool fast = s >= 0x1p-100f && s <= 0x1p+100f;
+    const float r = fast ? 1.0f / s : 0.0f;
 
-    constexpr int row_div = ABITS == 8 ? 1 : 2;
-    uint8_t* cr = codes + int64_t(m) * (K / row_div);
+    // Codes.  |h| <= amax and s is amax / qmax rounded, so |h / s| stays below
+    // qmax + 1/2 and round-half-even never leaves [-qmax, qmax]: the clamp of
+    // the definition is implied and not executed.
+    if (active) {
 #pragma unroll
-    for (int p = 0; p < P; ++p) {
-        const int c = p * T + tid;
-        if (c < nchunks) {
-            int q[8];
+        for (int grp = 0; grp < E / 16; ++grp) {
+            uint32_t t[16];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                float r = s > 0.0f ? rintf(v[p][i] / s) : 0.0f;
-                r = fminf(fmaxf(r, float(-qmax)), float(qmax));
-                q[i] = int(r);
+            for (int i = 0; i < 16; ++i) {
+                const float h = v[16 * grp + i];
+                float qf;
+                if (fast) {
+                    const float q0 = h * r;
+                    const float rem = __builtin_fmaf(-s, q0, h);
+                    qf = __builtin_fmaf(rem, r, q0);
+                } else {
+                    qf = s > 0.0f ? h / s : 0.0f;
+                }
+                t[i] = round_to_code_bits(qf);
             }
             if (ABITS == 8) {
-                uint2 o;
-                o.x = (uint32_t(q[0]) & 0xFF) | ((uint32_t(q[1]) & 0xFF) << 8) | ((uint32_t(q[2]) & 0xFF) << 16) |
-                      (uint32_t(q[3]) << 24);
-                o.y = (uint32_t(q[4]) & 0xFF) | ((uint32_t(q[5]) & 0xFF) << 8) | ((uint32_t(q[6]) & 0xFF) << 16) |
-                      (uint32_t(q[7]) << 24);
-                *reinterpret_cast<uint2*>(cr + 8 * c) = o;
-            } else {
-                uint32_t o = 0;
+                uint32_t w[4];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) o |= (uint32_t(q[i]) & 0xF) << (4 * i);
-                *reinterpret_cast<uint32_t*>(cr + 4 * c) = o;
+                for (int i = 0; i < 4; ++i) {
+                    // byte 0 of t[4i .. 4i+3] -> one dword
+                    const uint32_t lo = __builtin_amdgcn_perm(t[4 * i + 1], t[4 * i + 0], 0x0C0C0400u);
+                    const uint32_t hi = __builtin_amdgcn_perm(t[4 * i + 3], t[4 * i + 2], 0x0C0C0400u);
+                    w[i] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+                }
+                *reinterpret_cast<uint4*>(codes + int64_t(m) * K + E * c + 16 * grp) = make_uint4(w[0], w[1], w[2], w[3]);
+            } else {
+                uint32_t w[2];
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    uint32_t acc = 0;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) acc |= (t[8 * i + j] & 0xFu) << (4 * j);
+                    w[i] = acc;
+                }
+                *reinterpret_cast<uint2*>(codes + int64_t(m) * (K / 2) + (E / 2) * c + 8 * grp) = make_uint2(w[0], w[1]);
             }
         }
     }
-    if (tid == 0) act_scale[m] = s;
+    if (c == 0) act_scale[m] = s;
 }
 
-template <int ABITS>
-hipError_t launch_p(int P, dim3 grid, dim3 block, hipStream_t st, const PrologueArgs& a, float rs) {
-#define FQ_PRO_CASE(PP)                                                                                     \
-    case PP:                                                                                                \
-        hipLaunchKernelGGL((prologue_kernel<PP, ABITS>), grid, block, 0, st, a.x, a.K, a.ldx, a.gamma, a.eps, \
-                           a.ascale, a.fold_after, a.hblock, rs, a.codes, a.act_scale);                     \
-        break;
-    switch (P) {
-        FQ_PRO_CASE(1)
-        FQ_PRO_CASE(2)
-        FQ_PRO_CASE(3)
-        FQ_PRO_CASE(4)
-        FQ_PRO_CASE(5)
-        FQ_PRO_CASE(6)
-        FQ_PRO_CASE(7)
-        FQ_PRO_CASE(8)
-        default:
-            return hipErrorInvalidValue;
-    }
-#undef FQ_PRO_CASE
+template <int E, int ABITS, bool NORM, int AMODE, int LOG2B>
+hipError_t launch_e(dim3 grid, dim3 block, hipStream_t st, const PrologueArgs& a, float rs) {
+    hipLaunchKernelGGL((prologue_kernel<E, ABITS, NORM, AMODE, LOG2B>), grid, block, 0, st, a.x, a.K, a.ldx, a.gamma,
+                       a.eps, a.ascale, rs, a.codes, a.act_scale);
     return hipGetLastError();
+}
+
+template <int E, int ABITS, bool NORM, int AMODE>
+hipError_t launch_b(int log2b, dim3 grid, dim3 block, hipStream_t st, const PrologueArgs& a, float rs) {
+    switch (log2b) {
+        case 0: return launch_e<E, ABITS, NORM, AMODE, 0>(grid, block, st, a, rs);
+        case 1: return launch_e<E, ABITS, NORM, AMODE, 1>(grid, block, st, a, rs);
+        case 2: return launch_e<E, ABITS, NORM, AMODE, 2>(grid, block, st, a, rs);
+        case 3: return launch_e<E, ABITS, NORM, AMODE, 3>(grid, block, st, a, rs);
+        case 4: return launch_e<E, ABITS, NORM, AMODE, 4>(grid, block, st, a, rs);
+        case 5: return launch_e<E, ABITS, NORM, AMODE, 5>(grid, block, st, a, rs);
+        case 6: return launch_e<E, ABITS, NORM, AMODE, 6>(grid, block, st, a, rs);
+        case 7: return launch_e<E, ABITS, NORM, AMODE, 7>(grid, block, st, a, rs);
+        case 8: return launch_e<E, ABITS, NORM, AMODE, 8>(grid, block, st, a, rs);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int E, int ABITS>
+hipError_t launch_modes(dim3 grid, dim3 block, hipStream_t st, const PrologueArgs& a, float rs) {
+    int log2b = 0;
+    while ((1 << log2b) < a.hblock) ++log2b;
+    const int amode = a.ascale ? (a.fold_after ? 2 : 1) : 0;
+    if (a.gamma) {
+        if (amode == 0) return launch_b<E, ABITS, true, 0>(log2b, grid, block, st, a, rs);
+        if (amode == 1) return launch_b<E, ABITS, true, 1>(log2b, grid, block, st, a, rs);
+        return launch_b<E, ABITS, true, 2>(log2b, grid, block, st, a, rs);
+    }
+    if (amode == 0) return launch_b<E, ABITS, false, 0>(log2b, grid, block, st, a, rs);
+    if (amode == 1) return launch_b<E, ABITS, false, 1>(log2b, grid, block, st, a, rs);
+    return launch_b<E, ABITS, false, 2>(log2b, grid, block, st, a, rs);
 }
 
 }  // namespace
 
+// 32 values per lane (one pass of at most 1024 lanes up to K = 32768), 64 beyond.
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t stream) {
-    const int nchunks = a.K / 8;
-    const int P = (nchunks + kMaxThreads - 1) / kMaxThreads;
-    int T = (nchunks + P - 1) / P;
-    T = (T + 63) / 64 * 64;
+    const int E = a.K > 32768 ? 64 : 32;
+    const int nlanes = a.K / E;
+    const int T = (nlanes + 63) / 64 * 64;
+    if (T > kMaxThreads) return hipErrorInvalidValue;
     const float rs = float(1.0 / std::sqrt(double(a.hblock)));
     dim3 grid(a.M), block(T);
-    return a.abits == 8 ? launch_p<8>(P, grid, block, stream, a, rs) : launch_p<4>(P, grid, block, stream, a, rs);
+    if (E == 32)
+        return a.abits == 8 ? launch_modes<32, 8>(grid, block, stream, a, rs) : launch_modes<32, 4>(grid, block, stream, a, rs);
+    return a.abits == 8 ? launch_modes<64, 8>(grid, block, stream, a, rs) : launch_modes<64, 4>(grid, block, stream, a, rs);
 }
 
 }  // namespace fq
