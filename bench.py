@@ -173,16 +173,41 @@ def cpu_baseline(name, min_seconds=10.0, max_reps=400):
                        f"{len(times)} repetitions ({sum(times):.1f} s), median {t * 1e3:.1f} ms; weights packed once")
 
 
-def load_traffic(kernel_key):
-    """HBM traffic of the dominant kernel from the committed rocprofv3 counter summary, if present."""
+def gemm_bytes(wl):
+    """Bytes the GEMM must move at least once: both code matrices, both scale
+    vectors, the bf16 output (and the bf16 residual when there is one)."""
+    n = wl.M * wl.K * wl.abits // 8 + wl.N * wl.K * wl.wbits // 8 + 4 * (wl.M + wl.N) + 2 * wl.M * wl.N
+    return n + (2 * wl.M * wl.N if wl.residual is not None else 0)
+
+
+def copy_probe(nbytes=256 << 20):
+    """One plain device copy kernel of known size (reads and writes nbytes): the
+    scale for the FETCH_SIZE / WRITE_SIZE counters of a profiled run."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.mul(src, 1.0, out=dst)  # one elementwise kernel: nbytes in, nbytes out
+    torch.cuda.synchronize()
+    del src, dst
+    return nbytes
+
+
+def load_traffic(kernel_key, sources):
+    """Scaled FETCH_SIZE + WRITE_SIZE bytes per launch of a kernel from the committed
+    rocprofv3 counter summary; None if absent or taken on other kernel sources."""
+    import hashlib
     p = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
         return None
-    try:
-        d = json.load(open(p))
-        return d.get(kernel_key)
-    except Exception:
+    e = json.load(open(p)).get(kernel_key)
+    if e is None:
         return None
+    h = hashlib.sha256()
+    for src in sources:
+        with open(os.path.join(ROOT, "w4a4_integer_gemm_amd", "csrc", src), "rb") as f:
+            h.update(f.read())
+    return e["bytes"] if h.hexdigest() == e.get("source_sha256") else None
 
 
 def main():
@@ -193,6 +218,8 @@ def main():
     ap.add_argument("--workload", default="qkv_w8a8")
     ap.add_argument("--no-secondary", action="store_true", help="skip the down-projection and decode lines")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run one 256 MiB elementwise copy kernel (scale for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} requested, but this build measures one GPU only: the FoldQuant "
@@ -211,7 +238,9 @@ def main():
     achieved = r["ops"] / (r["ms_gemm"] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": "gemm_kernel<8,8> (fq_gemm, MFMA i8)", "achieved": achieved,
                 "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_INT8_TOPS,
-                "traffic": load_traffic(f"gemm:{args.workload}")}
+                "traffic": load_traffic(f"gemm:{args.workload}", ("fq_gemm.hip", "fq_device.h")),
+                "traffic_unit": "bytes per launch (scaled FETCH_SIZE + WRITE_SIZE)",
+                "algorithmic_bytes": gemm_bytes(wl)}
     secondary = []
     if not args.no_secondary:
         for name in ("down_w8a8",):
@@ -229,6 +258,7 @@ def main():
                               "ms_gemv": d["ms_gemv"], "algorithmic_bytes": d["bytes"],
                               "weights": "rotated over 5 device copies (679 MB) to defeat the Infinity Cache"})
         torch.cuda.empty_cache()
+    probe = copy_probe() if args.copy_probe else None
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.workload)
     out = {
         "metric": METRIC,
@@ -254,6 +284,8 @@ def main():
         "cpu_baseline": cpu,
         "secondary": secondary,
     }
+    if probe:
+        out["copy_probe_bytes"] = probe
     print(json.dumps(out), flush=True)
     if not r["parity_ok"]:
         print("bench.py: parity control FAILED on the timed buffers", file=sys.stderr)

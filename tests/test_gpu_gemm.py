@@ -99,3 +99,24 @@ def test_gemm_every_tile_shape(tile, bits, monkeypatch):
                                                         residual=True)
         assert np.array_equal(acc, acc_ref), f"{tile}: {np.count_nonzero(acc != acc_ref)} accumulators differ"
         assert_y_elementwise(yg, yf, acc_ref, sa, sw, b, res, what=f"{tile} M{M} N{N} K{K}")
+
+
+GEMV_SHAPES = [
+    # M, N, K: the GEMV splits K over 1..8 waves of a workgroup and walks each
+    # wave's share in batches; these cover one and several batches, shares that
+    # do not divide K evenly, a last wave with nothing to do, and M on both
+    # sides of 16
+    (1, 24, 1408), (2, 40, 1152), (15, 8, 640), (16, 72, 2304), (17, 24, 896),
+    (31, 16, 4608), (32, 8, 18944), (1, 3592, 3584), (16, 8, 65536), (3, 2056, 8192),
+]
+
+
+@pytest.mark.parametrize("shape", GEMV_SHAPES, ids=lambda s: "M{}_N{}_K{}".format(*s))
+@pytest.mark.parametrize("bits", [(8, 8), (4, 4), (8, 4), (4, 8)], ids=lambda b: "A{}W{}".format(*b))
+def test_gemv_split_k_shapes(shape, bits):
+    M, N, K = shape
+    log(f"gemv M={M} N={N} K={K} A{bits[0]}W{bits[1]}")
+    acc, acc_ref, yg, yf, sa, sw, b, res = run_gemm(M, N, K, bits[0], bits[1], seed=M + N + K, bias=True,
+                                                    residual=(M % 2 == 0))
+    assert np.array_equal(acc, acc_ref), f"{np.count_nonzero(acc != acc_ref)} accumulators differ"
+    assert_y_elementwise(yg, yf, acc_ref, sa, sw, b, res, what=f"gemv M{M} N{N} K{K}")

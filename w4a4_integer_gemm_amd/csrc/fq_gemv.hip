@@ -2,11 +2,18 @@
 //
 // For decode-sized M the layer is bound by reading the weight codes once from
 // HBM (the SYCL commit of the vla.cpp FoldQuant page also switches to a GEMV
-// for M <= 32).  Each wave owns 16 weight rows and walks the whole K: per
-// 64-deep step a lane loads 16 bytes (8 for 4-bit) of one row, and the
-// v_mfma_i32_16x16x64_i8 consumes them against the tokens' codes (tokens as
-// the 16-wide B operand; M > 16 takes a second MFMA).  U steps are loaded
-// before any is consumed so that each wave keeps U loads in flight.
+// for M <= 32).  A workgroup owns R groups of 16 weight rows and splits K
+// across its S waves; v_mfma_i32_16x16x64_i8 takes 16 rows as its A operand
+// and up to 16 tokens as B (M > 16 takes a second MFMA per step).
+//
+// Unit of work: one 16-byte weight load per lane, i.e. 64 k of 8-bit codes or
+// 128 k of 4-bit codes.  Lane l serves row l % 16 and the k quarter q = l / 16
+// of the unit.  A wave issues the loads of up to C units back to back (with
+// each unit's activation codes, which L2 serves) and only then consumes them,
+// so a wave has its whole share of the row group in flight at once: with only
+// N / 16 row groups in a decode layer, per-wave depth is what keeps HBM busy.
+// The S partial sums of each 16 x 16 output tile meet in LDS, and one wave
+// per tile runs the epilogue.
 #include <hip/hip_runtime.h>
 
 #include "fq_device.h"
@@ -15,93 +22,185 @@
 namespace fq {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
-constexpr int kUnroll = 8;
+constexpr int kMaxWaves = 8;
 
-template <int ABITS, int WBITS, int MT>
-__global__ __launch_bounds__(kThreads) void gemv_kernel(GemmArgs g) {
-    constexpr int wlane = WBITS == 8 ? 16 : 8;  // bytes per lane per step
-    constexpr int alane = ABITS == 8 ? 16 : 8;
-    constexpr int wrow = WBITS == 8 ? 64 : 32;  // bytes per row per step
-    constexpr int arow = ABITS == 8 ? 64 : 32;
+// k per unit and the bytes of one lane's activation codes per unit.
+template <int ABITS, int WBITS>
+struct Unit {
+    static constexpr int K = WBITS == 8 ? 64 : 128;
+    static constexpr int WROW = K * WBITS / 8;       // weight bytes per row per unit (64)
+    static constexpr int AROW = K * ABITS / 8;       // activation bytes per token per unit
+    static constexpr int ALANE = AROW / 4;           // 8, 16 or 32
+    static constexpr int AREGS = ALANE > 16 ? 2 : 1; // 16-byte registers per lane
+};
+
+// One lane's activation codes of one unit (8, 16 or 32 bytes).
+struct ActReg {
+    uint4 v[2];
+};
+
+template <int ABITS, int WBITS>
+__device__ __forceinline__ void load_act(ActReg& a, const uint8_t* p, bool ok) {
+    using U = Unit<ABITS, WBITS>;
+    a.v[0] = make_uint4(0, 0, 0, 0);
+    a.v[1] = make_uint4(0, 0, 0, 0);
+    if (ok) {
+        if (U::ALANE == 8) {
+            const uint2 t = *reinterpret_cast<const uint2*>(p);
+            a.v[0] = make_uint4(t.x, t.y, 0, 0);
+        } else {
+            a.v[0] = *reinterpret_cast<const uint4*>(p);
+            if (U::AREGS == 2) a.v[1] = *reinterpret_cast<const uint4*>(p + 16);
+        }
+    }
+}
+
+// acc += the unit's product; w = the lane's 16 weight bytes.
+//  8-bit weights: one MFMA over k = 16 q + [0, 16) of the unit.
+//  4-bit weights: the lane's 32 nibbles are k = 32 q + [0, 32); MFMA j takes
+//  bytes 8 j .. 8 j + 7 of both operands, k = 32 q + 16 j + [0, 16).
+template <int ABITS, int WBITS>
+__device__ __forceinline__ v4i unit_mfma(const uint4 w, const ActReg& a, v4i acc) {
+    if (WBITS == 8) {
+        if (ABITS == 8) return mfma16x16x64(frag_from_bytes(w), frag_from_bytes(a.v[0]), acc);
+        return mfma16x16x64(frag_from_bytes_nibble_order(w), frag_from_nibbles(make_uint2(a.v[0].x, a.v[0].y)),
+                            acc);
+    }
+    const v4i w0 = frag_from_nibbles(make_uint2(w.x, w.y));
+    const v4i w1 = frag_from_nibbles(make_uint2(w.z, w.w));
+    if (ABITS == 4) {
+        acc = mfma16x16x64(w0, frag_from_nibbles(make_uint2(a.v[0].x, a.v[0].y)), acc);
+        return mfma16x16x64(w1, frag_from_nibbles(make_uint2(a.v[0].z, a.v[0].w)), acc);
+    }
+    acc = mfma16x16x64(w0, frag_from_bytes_nibble_order(a.v[0]), acc);
+    return mfma16x16x64(w1, frag_from_bytes_nibble_order(a.v[1]), acc);
+}
+
+// grid: one workgroup per R groups of 16 rows; block: S waves; `per` units per wave.
+// Each wave loads a unit's activation codes once and uses them for its R row
+// groups, which keeps the activation re-reads (from L2) at M / (16 R) of the
+// weight bytes.
+template <int ABITS, int WBITS, int R, int MT, int C>
+__global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(GemmArgs g, int per) {
+    using U = Unit<ABITS, WBITS>;
+    constexpr int kTiles = R * MT;
+    __shared__ v4i red[kMaxWaves][kTiles][64];
+
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int n0 = (blockIdx.x * kWaves + wave) * 16;
-    if (n0 >= g.N) return;  // whole wave
-    const int64_t ldw = WBITS == 8 ? g.K : g.K / 2;
-    const int64_t lda = ABITS == 8 ? g.K : g.K / 2;
-    const int nk = g.K / 64;
-    const int row = n0 + (lane & 15);
-    const bool row_ok = row < g.N;
-    const uint8_t* wp = g.w + int64_t(row_ok ? row : 0) * ldw + (lane >> 4) * wlane;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int S = blockDim.x >> 6;
+    const int q = lane >> 4;
+    const int n0 = blockIdx.x * 16 * R;
+    const int nu = g.K / U::K;
+    const int u_begin = wave * per;
+    const int u_end = u_begin + per < nu ? u_begin + per : nu;
+
+    const int64_t ldw = int64_t(g.K) * WBITS / 8;
+    const uint8_t* wp[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        int row = n0 + 16 * r + (lane & 15);
+        row = row < g.N ? row : g.N - 1;  // rows past N load a valid row; their outputs are not stored
+        wp[r] = g.w + int64_t(row) * ldw + q * 16;
+    }
+    const int64_t lda = int64_t(g.K) * ABITS / 8;
     const uint8_t* ap[MT];
     bool tok_ok[MT];
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
         const int tok = t * 16 + (lane & 15);
         tok_ok[t] = tok < g.M;
-        ap[t] = g.act + int64_t(tok_ok[t] ? tok : 0) * lda + (lane >> 4) * alane;
+        ap[t] = g.act + int64_t(tok_ok[t] ? tok : 0) * lda + q * U::ALANE;
     }
 
-    v4i acc[MT];
+    v4i acc[R][MT];
 #pragma unroll
-    for (int t = 0; t < MT; ++t) acc[t] = v4i{0, 0, 0, 0};
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[r][t] = v4i{0, 0, 0, 0};
 
-    for (int k0 = 0; k0 < nk; k0 += kUnroll) {
-        uint4 wv[kUnroll];
+    for (int u0 = u_begin; u0 < u_end; u0 += C) {
+        uint4 wv[C][R];
+        ActReg av[C][MT];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            wv[u] = make_uint4(0, 0, 0, 0);
-            if (k0 + u < nk && row_ok) {
-                const uint8_t* p = wp + int64_t(k0 + u) * wrow;
-                if (WBITS == 8) {
-                    wv[u] = load_stream16(p);
-                } else {
-                    const uint2 v = load_stream8(p);
-                    wv[u].x = v.x;
-                    wv[u].y = v.y;
-                }
+        for (int c = 0; c < C; ++c) {
+            if (u0 + c < u_end) {  // wave-uniform
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+                    wv[c][r] = *reinterpret_cast<const uint4*>(wp[r] + int64_t(u0 + c) * U::WROW);
+#pragma unroll
+                for (int t = 0; t < MT; ++t)
+                    load_act<ABITS, WBITS>(av[c][t], ap[t] + int64_t(u0 + c) * U::AROW, tok_ok[t]);
             }
         }
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            if (k0 + u < nk) {
-                v4i fw;
-                if (WBITS == 8) {
-                    fw = ABITS == 8 ? frag_from_bytes(wv[u]) : frag_from_bytes_nibble_order(wv[u]);
-                } else {
-                    fw = frag_from_nibbles(make_uint2(wv[u].x, wv[u].y));
-                }
+        for (int c = 0; c < C; ++c) {
+            if (u0 + c < u_end) {
 #pragma unroll
-                for (int t = 0; t < MT; ++t) {
-                    v4i fa = v4i{0, 0, 0, 0};
-                    if (tok_ok[t]) fa = Frag<ABITS, WBITS>::load(ap[t] + int64_t(k0 + u) * arow);
-                    acc[t] = mfma16x16x64(fw, fa, acc[t]);
-                }
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int t = 0; t < MT; ++t) acc[r][t] = unit_mfma<ABITS, WBITS>(wv[c][r], av[c][t], acc[r][t]);
             }
         }
     }
 
+    // lane holds D[n = n0 + 16 r + 4 q + i][m = 16 t + lane % 16] of tile (r, t)
     constexpr int shift = AccShift<ABITS, WBITS>::value;
-    const int n = n0 + (lane >> 4) * 4;
-    if (n >= g.N) return;
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
+    auto store = [&](const v4i a, int r, int t) {
+        const int n = n0 + 16 * r + q * 4;
         const int m = t * 16 + (lane & 15);
-        if (m < g.M)
-            store_out4(acc[t], shift, m, n, g.act_scale[m], g.wscale, g.bias, g.residual, g.ldr, g.y, g.ldy, g.acc,
-                       g.N);
+        if (n < g.N && m < g.M)
+            store_out4(a, shift, m, n, g.act_scale[m], g.wscale, g.bias, g.residual, g.ldr, g.y, g.ldy, g.acc, g.N);
+    };
+    if (S == 1) {  // block-uniform
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int t = 0; t < MT; ++t) store(acc[r][t], r, t);
+        return;
     }
+    // tile i = (r, t) = (i / MT, i % MT): wave i sums the S partials of tile i and stores it
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) red[wave][r * MT + t][lane] = acc[r][t];
+    __syncthreads();
+    if (wave >= kTiles) return;
+    v4i sum = red[0][wave][lane];
+    for (int w = 1; w < S; ++w) sum += red[w][wave][lane];
+    store(sum, wave / MT, wave % MT);
 }
 
+// Waves per workgroup: enough that a wave's share fits one batch of C units,
+// more while the layer has few workgroups and each wave keeps >= 4 units.
+// At least R * MT waves so that every output tile has a wave to store it.
+int split_waves(int nu, int groups, int C, int tiles) {
+    int S = 1;
+    while (S < kMaxWaves && (nu + S - 1) / S > C) S *= 2;
+    while (S < kMaxWaves && int64_t(groups) * S < 4096 && (nu + 2 * S - 1) / (2 * S) >= 4) S *= 2;
+    while (S < tiles && S > 1) S *= 2;
+    return S;
+}
+
+template <int ABITS, int WBITS, int R, int MT, int C>
+void launch_cfg(const GemmArgs& g, hipStream_t st) {
+    const int nu = g.K / Unit<ABITS, WBITS>::K;
+    const int groups = (g.N + 16 * R - 1) / (16 * R);
+    const int S = split_waves(nu, groups, C, R * MT);
+    const int per = (nu + S - 1) / S;
+    hipLaunchKernelGGL((gemv_kernel<ABITS, WBITS, R, MT, C>), dim3(groups), dim3(64 * S), 0, st, g, per);
+}
+
+// Row groups per wave grow with M so that the activation re-reads stay a
+// small fraction of the weight stream.
 template <int ABITS, int WBITS>
 void launch_bits(const GemmArgs& g, hipStream_t st) {
-    dim3 grid((g.N + kWaves * 16 - 1) / (kWaves * 16)), block(kThreads);
-    if (g.M <= 16)
-        hipLaunchKernelGGL((gemv_kernel<ABITS, WBITS, 1>), grid, block, 0, st, g);
+    if (g.M <= 4)
+        launch_cfg<ABITS, WBITS, 1, 1, 16>(g, st);
+    else if (g.M <= 16)
+        launch_cfg<ABITS, WBITS, 2, 1, 8>(g, st);
     else
-        hipLaunchKernelGGL((gemv_kernel<ABITS, WBITS, 2>), grid, block, 0, st, g);
+        launch_cfg<ABITS, WBITS, 2, 2, 8>(g, st);
 }
 
 }  // namespace
