@@ -54,7 +54,7 @@ SHAPES = [
     (300, 1000, 2048), (816, 264, 1024),
 ]
 
-TILES = ["128x128", "128x144", "128x112", "256x128", "128x256", "64x128"]
+TILES = ["128x128", "128x144", "128x112", "128x96", "64x128", "64x224", "64x256", "64x288"]
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "M{}_N{}_K{}".format(*s))

@@ -111,40 +111,70 @@ __device__ __forceinline__ v4i mfma16x16x64(v4i a, v4i b, v4i c) {
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
-// Epilogue for 4 consecutive output features n..n+3 of token m.
-__device__ __forceinline__ void store_out4(const v4i acc, int shift, int m, int n, float sa,
-                                           const float* __restrict__ wscale, const float* __restrict__ bias,
-                                           const uint16_t* __restrict__ residual, int64_t ldr,
-                                           uint16_t* __restrict__ y, int64_t ldy, int32_t* __restrict__ acc_out,
-                                           int N) {
-    const float4 sw = *reinterpret_cast<const float4*>(wscale + n);
-    int a0 = acc[0] >> shift, a1 = acc[1] >> shift, a2 = acc[2] >> shift, a3 = acc[3] >> shift;
-    float t0 = float(a0) * (sa * sw.x);
-    float t1 = float(a1) * (sa * sw.y);
-    float t2 = float(a2) * (sa * sw.z);
-    float t3 = float(a3) * (sa * sw.w);
-    if (bias) {
-        const float4 b = *reinterpret_cast<const float4*>(bias + n);
-        t0 = t0 + b.x;
-        t1 = t1 + b.y;
-        t2 = t2 + b.z;
-        t3 = t3 + b.w;
+// Epilogue for a wave's TN x TM accumulator tiles: tile (i, ii) holds output
+// features n[i] + 4 (lane / 16) + r (r = 0..3, the four accumulator values) of
+// token m[ii] + lane % 16, with n[i] and m[ii] already including the lane's part:
+//   y[m][n] = bf16_rne(float(acc >> shift) * (s_m * s_n) [+ bias_n] [+ residual_mn])
+// in float32, each step rounded (no contraction); acc_out, when given, receives
+// the exact integer sums.  Every operand is loaded before the first store: on
+// gfx9 stores count in the same vector-memory counter as loads, so a load placed
+// after a store would wait for that store to complete.
+template <int TN, int TM>
+__device__ __forceinline__ void store_tiles(const v4i (&acc)[TN][TM], int shift, const int (&m)[TM], const int (&n)[TN],
+                                            int M, int N, const float* __restrict__ act_scale,
+                                            const float* __restrict__ wscale, const float* __restrict__ bias,
+                                            const uint16_t* __restrict__ residual, int64_t ldr,
+                                            uint16_t* __restrict__ y, int64_t ldy, int32_t* __restrict__ acc_out) {
+    float sa[TM];
+#pragma unroll
+    for (int ii = 0; ii < TM; ++ii) sa[ii] = m[ii] < M ? act_scale[m[ii]] : 0.0f;
+    float4 sw[TN], bs[TN];
+#pragma unroll
+    for (int i = 0; i < TN; ++i) {
+        const bool ok = n[i] < N;
+        sw[i] = ok ? *reinterpret_cast<const float4*>(wscale + n[i]) : make_float4(0.f, 0.f, 0.f, 0.f);
+        bs[i] = (bias && ok) ? *reinterpret_cast<const float4*>(bias + n[i]) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    if (residual) {
-        const uint2 r = *reinterpret_cast<const uint2*>(residual + int64_t(m) * ldr + n);
-        t0 = t0 + bf16_lo(r.x);
-        t1 = t1 + bf16_hi(r.x);
-        t2 = t2 + bf16_lo(r.y);
-        t3 = t3 + bf16_hi(r.y);
-    }
-    uint2 o;
-    o.x = f32_to_bf16(t0) | (f32_to_bf16(t1) << 16);
-    o.y = f32_to_bf16(t2) | (f32_to_bf16(t3) << 16);
-    *reinterpret_cast<uint2*>(y + int64_t(m) * ldy + n) = o;
-    if (acc_out) {
-        int4 v = make_int4(a0, a1, a2, a3);
-        *reinterpret_cast<int4*>(acc_out + int64_t(m) * N + n) = v;
-    }
+    uint2 rs[TN][TM];
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int ii = 0; ii < TM; ++ii)
+            rs[i][ii] = (residual && n[i] < N && m[ii] < M)
+                            ? *reinterpret_cast<const uint2*>(residual + int64_t(m[ii]) * ldr + n[i])
+                            : make_uint2(0, 0);
+    // one wait for all of them, outside any branch, so that no wait is placed
+    // behind a store below (vmcnt(0), other counters untouched)
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+#pragma unroll
+    for (int ii = 0; ii < TM; ++ii)
+#pragma unroll
+        for (int i = 0; i < TN; ++i) {
+            if (m[ii] >= M || n[i] >= N) continue;
+            const int a0 = acc[i][ii][0] >> shift, a1 = acc[i][ii][1] >> shift;
+            const int a2 = acc[i][ii][2] >> shift, a3 = acc[i][ii][3] >> shift;
+            float t0 = float(a0) * (sa[ii] * sw[i].x);
+            float t1 = float(a1) * (sa[ii] * sw[i].y);
+            float t2 = float(a2) * (sa[ii] * sw[i].z);
+            float t3 = float(a3) * (sa[ii] * sw[i].w);
+            if (bias) {
+                t0 = t0 + bs[i].x;
+                t1 = t1 + bs[i].y;
+                t2 = t2 + bs[i].z;
+                t3 = t3 + bs[i].w;
+            }
+            if (residual) {
+                t0 = t0 + bf16_lo(rs[i][ii].x);
+                t1 = t1 + bf16_hi(rs[i][ii].x);
+                t2 = t2 + bf16_lo(rs[i][ii].y);
+                t3 = t3 + bf16_hi(rs[i][ii].y);
+            }
+            uint2 o;
+            o.x = f32_to_bf16(t0) | (f32_to_bf16(t1) << 16);
+            o.y = f32_to_bf16(t2) | (f32_to_bf16(t3) << 16);
+            *reinterpret_cast<uint2*>(y + int64_t(m[ii]) * ldy + n[i]) = o;
+            if (acc_out) *reinterpret_cast<int4*>(acc_out + int64_t(m[ii]) * N + n[i]) = make_int4(a0, a1, a2, a3);
+        }
 }
 
 }  // namespace fq

@@ -1,35 +1,34 @@
 // FoldQuant integer GEMM with the fused dequant/residual epilogue on gfx950.
 //
-// acc[m][n] = sum_k qa[m][k] * qw[n][k] on v_mfma_i32_16x16x64_i8 (the vla.cpp
+// acc[m][n] = sum_k qa[m][k] * qw[n][k] on v_mfma_i32_32x32x32_i8 (the vla.cpp
 // FoldQuant page's "gemm" node: integer GEMM against per-row scaled INT8/INT4
 // weight codes with per-shape tiling and the residual add in the epilogue).
 // Integer sums are exact in any order, so tile shape and k order are free.
 //
-// Structure (one 256-thread workgroup = 4 waves per BM x BN output tile):
-//   - k advances in stages of 128.  A stage of the two operand tiles is copied
-//     global -> LDS with global_load_lds_dwordx4 (no VGPR staging); NS stages
-//     live in an LDS ring so NS-1 stages of loads are in flight while the MFMAs
-//     consume the oldest one.  One s_barrier per stage; the waits count each
-//     wave's own outstanding loads (vmcnt), so no wave waits for loads that a
-//     later stage issued.
-//   - Each 1 KB chunk of a stage is one wave-wide load: lane l fetches 16 bytes
-//     of row (l % 16).  The chunk is therefore already in MFMA operand order
-//     (lane l reads bytes 16*l .. 16*l+15), so operand reads are conflict-free
-//     ds_read_b128.
-//   - The MFMA's A operand is a 16-row weight fragment and its B operand a
-//     16-token activation fragment, so each lane ends with four consecutive
-//     output features of one token: one 8-byte bf16 store in the epilogue.
+// Structure (one 256-thread workgroup = 4 waves per BM x BNS output tile):
+//   - MFMA: v_mfma_i32_32x32x32_i8 with the weight fragment (32 rows n) as the
+//     A operand and the token fragment (32 tokens m) as B; lane l holds token
+//     l % 32 of the result and rows n = 8 g + 4 (l / 32) + i in register 4 g + i.
+//   - k advances in stages of 128 (256 with a 4-bit operand).  A stage of the
+//     two operand tiles is copied global -> LDS with global_load_lds_dwordx4 (no
+//     VGPR staging); NS stages live in an LDS ring, so NS-1 stages of loads are
+//     in flight while the MFMAs consume the oldest one.  One s_barrier per
+//     stage; the waits count each wave's own outstanding loads (vmcnt).
+//   - Waves 0/1 take tokens 0 .. BM/2-1 / BM/2 .. BM-1 and waves 0,1 / 2,3 take
+//     alternate 32-deep k steps of every stage (split k inside the workgroup),
+//     so each wave reads half the weight fragments a token-only split would.
+//     At the end the two k halves of a token block add up through LDS.
+//   - A tile computes BNC rows (BNS rounded up to 32); rows past BNS belong to
+//     the next tile and are not stored.
 //   - Rows past M or N are clamped to the last row when loading (their results
 //     are never stored), so no load is ever masked or out of bounds.
 //   - The workgroup -> tile map is XCD aware: consecutive dispatch ids land on
 //     different XCDs, so tiles are renumbered to give each XCD a compact block
 //     of the output that shares operand rows in its own L2.
 //
-// k order inside a 128-k stage (lane l, MFMA sub-step j in {0, 1}):
-//   both operands 8-bit: k = 64 j + 16 (l / 16) + [0, 16)
-//   otherwise:           k = 32 (l / 16) + 16 j + [0, 16)  (4-bit codes: the
-//     16 packed bytes of a lane hold both sub-steps; an 8-bit partner loads
-//     the same k and permutes its bytes into the nibble order of fq_device.h)
+// k order inside a stage (lane l, MFMA k step j): k = 32 j + 16 (l / 32) + [0, 16).
+// A 4-bit operand's 16 codes are 8 bytes, unpacked to bytes in registers; an
+// 8-bit partner permutes its bytes into the nibble order of fq_device.h.
 #include <hip/hip_runtime.h>
 
 #include <cstdlib>
@@ -44,27 +43,22 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// 16-byte-per-lane global -> LDS copy (global_load_lds_dwordx4): lane l's 16
-// bytes land at lds_dst + 16 l; lds_dst must be wave uniform (it goes to M0).
-// Written as inline asm so that the compiler does not wait for every
-// outstanding copy before each LDS read; completion is tracked explicitly
-// with wait_vmcnt and the stage barrier.  M0 is restored afterwards.  The
-// instruction has no VGPR result, only the address operand, which the
+// 16-byte-per-lane global -> LDS copy (global_load_lds_dwordx4, SGPR base +
+// 32-bit VGPR offset form): lane l reads base + voff and its 16 bytes land at
+// lds_dst + 16 l; lds_dst must be wave uniform (it is passed in M0).  Written
+// as inline asm so that the compiler does not wait for every outstanding copy
+// before each LDS read; completion is tracked explicitly with wait_vmcnt and
+// the stage barrier.  The s_nop covers the M0-write -> LDS-DMA hazard.  The
+// instruction has no VGPR result, only the address operands, which the
 // hardware consumes at issue.
-__device__ __forceinline__ void copy16_to_lds(const uint8_t* gsrc, uint8_t* lds_dst) {
-    typedef __attribute__((address_space(3))) uint8_t lds_byte;
-    uint32_t a = uint32_t(reinterpret_cast<uintptr_t>((lds_byte*)lds_dst));
-    a = __builtin_amdgcn_readfirstlane(a);
-    uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %2\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, off\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "v"(gsrc), "s"(a)
-        : "memory");
+__device__ __forceinline__ void copy16_to_lds(const uint8_t* base, uint32_t voff, uint32_t lds_dst) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(base), "{m0}"(lds_dst) : "memory");
+}
+
+// LDS byte address of a pointer into __shared__ memory (wave uniform).
+__device__ __forceinline__ uint32_t lds_address(const uint8_t* p) {
+    typedef __attribute__((address_space(3))) const uint8_t lds_byte;
+    return __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>((lds_byte*)p)));
 }
 
 // s_waitcnt vmcnt(n) leaving the other counters untouched (gfx9 encoding).
@@ -82,47 +76,64 @@ __device__ __forceinline__ void barrier_nofence() {
     asm volatile("" ::: "memory");
 }
 
-template <int ABITS, int WBITS, int BM_, int BN_, int WGM_, int WGN_, int NS_>
+template <int ABITS, int WBITS, int BM_, int BNS_, int BNC_, int NS_, int KS8 = 128>
 struct Cfg {
-    static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, NS = NS_;
-    static constexpr bool MIXED = ABITS != WBITS;
-    static constexpr int KS = (ABITS == 4 || WBITS == 4) ? 256 : 128;  // k per stage
-    static constexpr int NSUB = KS / 64;                                // MFMA steps per stage
+    // BM tokens x BNS stored weight rows per tile; BNC >= BNS rows are computed
+    // (a multiple of 32: the MFMA's row count); rows past BNS belong to the next
+    // tile and are discarded.
+    static constexpr int BM = BM_, BNS = BNS_, BNC = BNC_, NS = NS_;
+    static constexpr int KS = (ABITS == 4 || WBITS == 4) ? 256 : KS8;  // k per stage
+    static constexpr int NK32 = KS / 32;                                // MFMA k steps per stage
+    static constexpr int NSTEP = NK32 / 2;                              // per wave (k split over pairs)
     static constexpr int RA = KS * ABITS / 8, RW = KS * WBITS / 8;      // bytes per row per stage
-    static constexpr int FA = BM / 16, FW = BN / 16;                    // 16-row fragments
-    static constexpr int IA = 16 * RA / 1024, IW = 16 * RW / 1024;      // 1 KB loads per fragment
-    static constexpr int CA = FA * IA, CW = FW * IW, C = CA + CW;       // 1 KB loads per stage
+    static constexpr int CA = BM * RA / 1024, CW = BNC * RW / 1024;     // 1 KB loads per stage
+    static constexpr int C = CA + CW;
     static constexpr int STAGE = C * 1024;
     static constexpr int LDS = NS * STAGE;
-    static constexpr int WTM = BM / WGM, WTN = BN / WGN;
-    static constexpr int TM = WTM / 16, TN = WTN / 16;
+    static constexpr int TMF = BM / 64;   // 32-token fragments per wave
+    static constexpr int TN = BNC / 32;   // 32-row weight fragments per wave
+    static constexpr int TN0 = (TN + 1) / 2;  // output fragments stored by the k-half 0 wave
     static constexpr int NLO = C / 4, NHI = (C + 3) / 4;
-    static_assert(WGM * WGN == 4, "four waves");
-    static_assert(BM % (16 * WGM) == 0 && BN % (16 * WGN) == 0, "wave tiles of whole fragments");
+    static_assert(BM == 64 || BM == 128, "two waves of 32 or 64 tokens");
+    static_assert(BNC % 32 == 0 && BNC >= BNS, "computed rows in whole MFMA fragments");
+    static_assert((BM * RA) % 1024 == 0 && (BNC * RW) % 1024 == 0, "whole 1 KB loads");
     static_assert(LDS <= 163840, "LDS ring exceeds 160 KiB");
     static_assert(NS >= 3, "the ring needs a slot being filled, one ready and one being read");
     static_assert((NS - 2) * NHI < 64, "vmcnt range");
+    static_assert(LDS >= 2 * TMF * TN * 4096, "the split-k exchange reuses the ring");
 };
 
-// LDS layout of one 16-row fragment of an operand whose rows hold R bytes per
-// stage: 16-byte slot (rho, kc) sits at KC*rho + (kc ^ g(rho)), KC = R/16.  A
-// 1 KB load instruction covers whole rows (8 rows of 128 B or 4 of 256 B), so
-// every row segment it fetches is whole 128-byte lines; the xor keeps the 16
-// lanes of an MFMA operand read (16 rows, one kc) on 16 distinct slot columns.
-template <int R>
-__device__ __forceinline__ int slot_of(int rho, int kc) {
-    constexpr int KC = R / 16;
-    const int gx = KC == 8 ? ((rho >> 1) & 7) : (rho & 15);
-    return KC * rho + (kc ^ gx);
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ v16i mfma32x32x32(v4i a, v4i b, v16i c) {
+    return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
 }
 
-// LDS byte offset (inside a fragment) of lane `lane`'s operand for MFMA step j:
-// step j covers k = 64 j + 16 (lane / 16) + [0, 16) of the stage
+// LDS layout of an operand tile whose rows hold R bytes per stage: 16-byte slot
+// (rho, kc) sits at KC*rho + (kc ^ g(rho)), KC = R/16.  A 1 KB load covers
+// whole rows (16 rows of 64 B, 8 of 128 B or 4 of 256 B); the
+// xor keeps the 16 lanes that one ds_read_b128 phase serves (16 consecutive
+// rows, one kc) on 16 distinct groups of four banks.
+template <int R>
+__device__ __forceinline__ int slot_swizzle(int rho) {
+    constexpr int KC = R / 16;
+    static_assert(KC == 4 || KC == 8 || KC == 16, "rows of 64, 128 or 256 bytes");
+    return KC == 4 ? ((rho >> 2) & 3) : KC == 8 ? ((rho >> 1) & 7) : (rho & 15);
+}
+template <int R>
+__device__ __forceinline__ int slot_of(int rho, int kc) {
+    return (R / 16) * rho + (kc ^ slot_swizzle<R>(rho));
+}
+
+// LDS byte offset of lane `lane`'s 16-k operand chunk for MFMA k step j of a
+// stage, in the operand tile's first 32 rows (row 32 f + r is R * 32 f further:
+// the swizzle only uses the low 4 bits of the row).  Lane l serves row l % 32
+// and the k half h = l / 32: k = 32 j + 16 h + [0, 16).
 template <int BITS, int R>
 __device__ __forceinline__ int operand_offset(int lane, int j) {
-    const int rho = lane & 15;
-    if (BITS == 8) return 16 * slot_of<R>(rho, 4 * j + (lane >> 4));             // 16 k = 16 bytes
-    return 16 * slot_of<R>(rho, 2 * j + (lane >> 5)) + 8 * ((lane >> 4) & 1);  // 16 k = 8 bytes
+    const int rho = lane & 31, h = lane >> 5;
+    if (BITS == 8) return 16 * slot_of<R>(rho, 2 * j + h);  // 16 k = 16 bytes
+    return 16 * slot_of<R>(rho, j) + 8 * h;                 // 16 k = 8 bytes
 }
 
 template <int BITS, int PARTNER>
@@ -132,15 +143,24 @@ __device__ __forceinline__ v4i operand_from_lds(const uint8_t* p) {
     return PARTNER == 4 ? frag_from_bytes_nibble_order(v) : frag_from_bytes(v);
 }
 
-// global source of load instruction q (of a fragment) for `lane`: row rho of the
-// fragment and 16-byte column kc, inverse of slot_of
+// global source of 1 KB load q of an operand tile for `lane`: row rho of the
+// tile and 16-byte column kc, the inverse of slot_of
 template <int R>
 __device__ __forceinline__ void slot_source(int q, int lane, int& rho, int& kc) {
     constexpr int KC = R / 16;
     const int sigma = 64 * q + lane;
     rho = sigma / KC;
-    kc = (sigma % KC) ^ (KC == 8 ? ((rho >> 1) & 7) : (rho & 15));
+    kc = (sigma % KC) ^ slot_swizzle<R>(rho);
 }
+
+// Epilogue of one 32 x 32 output fragment held by a wave (v_mfma_i32_32x32x32
+// layout: lane l holds token m, and rows n = 8 g + 4 (l / 32) + i of register
+// 4 g + i).  The caller has loaded every operand already (see store_tiles in
+// fq_device.h for why the loads come first).
+struct Out4 {
+    float4 sw, bias;
+    uint2 res;
+};
 
 template <int ABITS, int WBITS, class CF>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m, int tiles_n) {
@@ -159,7 +179,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
         t = (blockIdx.x % 8) * per + blockIdx.x / 8;
     }
     const int tm = t % tiles_m, tn = t / tiles_m;
-    const int m0 = tm * CF::BM, n0 = tn * CF::BN;
+    const int m0 = tm * CF::BM, n0 = tn * CF::BNS;
     const int64_t lda = ABITS == 8 ? g.K : g.K / 2;
     const int64_t ldw = WBITS == 8 ? g.K : g.K / 2;
     // K is a multiple of 128; with a 4-bit operand a stage is 256 deep and the
@@ -169,65 +189,73 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
 
     // This wave's load instructions: c = wave + 4 i.  Waves with one fewer
     // instruction repeat their last one (same source, same LDS bytes), so every
-    // wave issues NHI loads per stage and the waits below are uniform.  A lane
-    // whose column would run past the end of a row (only in a half-deep last
-    // stage) re-reads bytes of its row's first 64; that LDS slot is never used.
-    const uint8_t* gp[CF::NHI];
-    int col[CF::NHI], gstep[CF::NHI], rowlen[CF::NHI], ldsoff[CF::NHI];
+    // wave issues NHI loads per stage and the waits below are uniform.  Each
+    // load reads row-block base (scalar, advanced per stage) + a fixed per-lane
+    // offset.  In a half-deep last stage a lane whose column would run past the
+    // end of its row reads bytes of the stage's first 64 instead; that LDS slot
+    // is never used.
+    const uint8_t* abase = g.act + int64_t(m0) * lda;
+    const uint8_t* wbase = g.w + int64_t(n0) * ldw;
+    uint32_t voff[CF::NHI], dlast[CF::NHI];
+    int ldsoff[CF::NHI];
+    bool is_act[CF::NHI];
 #pragma unroll
     for (int i = 0; i < CF::NHI; ++i) {
         int c = wave + 4 * i;
         if (c >= CF::C) c -= 4;
         ldsoff[i] = c * 1024;
-        int rho, kc;
+        int rho, kc, rowoff, half;
+        is_act[i] = c < CF::CA;
         if (c < CF::CA) {
-            slot_source<CF::RA>(c % CF::IA, lane, rho, kc);
-            int row = m0 + (c / CF::IA) * 16 + rho;
+            slot_source<CF::RA>(c, lane, rho, kc);
+            int row = m0 + rho;
             row = row < g.M ? row : g.M - 1;
-            gp[i] = g.act + int64_t(row) * lda;
-            gstep[i] = CF::RA;
-            rowlen[i] = int(lda);
+            rowoff = (row - m0) * int(lda);
+            half = CF::RA / 2;
         } else {
-            const int cw = c - CF::CA;
-            slot_source<CF::RW>(cw % CF::IW, lane, rho, kc);
-            int row = n0 + (cw / CF::IW) * 16 + rho;
+            slot_source<CF::RW>(c - CF::CA, lane, rho, kc);
+            int row = n0 + rho;
             row = row < g.N ? row : g.N - 1;
-            gp[i] = g.w + int64_t(row) * ldw;
-            gstep[i] = CF::RW;
-            rowlen[i] = int(ldw);
+            rowoff = (row - n0) * int(ldw);
+            half = CF::RW / 2;
         }
-        col[i] = 16 * kc;
+        const int col = 16 * kc;
+        voff[i] = uint32_t(rowoff + col);
+        dlast[i] = uint32_t((col < half ? col : (col & 63)) - col);  // rows are at least 64 bytes
     }
+    const uint32_t lds0 = lds_address(lds);
     auto dma = [&](int stage_idx, int slot, int i) {
-        int off = stage_idx * gstep[i] + col[i];
-        off = off < rowlen[i] ? off : (col[i] & 63);  // rows are at least 64 bytes
-        copy16_to_lds(gp[i] + off, lds + slot * CF::STAGE + ldsoff[i]);
+        const uint8_t* base = is_act[i] ? abase + int64_t(stage_idx) * CF::RA : wbase + int64_t(stage_idx) * CF::RW;
+        const uint32_t off = voff[i] + ((half_last && stage_idx == nk - 1) ? dlast[i] : 0u);
+        copy16_to_lds(base, off, lds0 + uint32_t(slot * CF::STAGE + ldsoff[i]));
     };
 
-    const int wm = wave % CF::WGM;  // wave's token block
-    const int wn = wave / CF::WGM;  // wave's weight-row block
-    int offa[CF::NSUB], offw[CF::NSUB];
+    // wave roles: tokens wm * BM/2 .. + BM/2 (TMF fragments of 32), all BNC
+    // weight rows (TN fragments), and the MFMA k steps j = 2 i + kh of every stage
+    const int wm = wave & 1;
+    const int kh = wave >> 1;
+    int offa[CF::NSTEP], offw[CF::NSTEP];
 #pragma unroll
-    for (int j = 0; j < CF::NSUB; ++j) {
-        offa[j] = operand_offset<ABITS, CF::RA>(lane, j) + wm * CF::TM * 16 * CF::RA;
-        offw[j] = operand_offset<WBITS, CF::RW>(lane, j) + CF::CA * 1024 + wn * CF::TN * 16 * CF::RW;
+    for (int i = 0; i < CF::NSTEP; ++i) {
+        offa[i] = operand_offset<ABITS, CF::RA>(lane, 2 * i + kh) + wm * CF::TMF * 32 * CF::RA;
+        offw[i] = operand_offset<WBITS, CF::RW>(lane, 2 * i + kh) + CF::CA * 1024;
     }
 
-    v4i acc[CF::TN][CF::TM];
+    v16i acc[CF::TN][CF::TMF];
 #pragma unroll
     for (int i = 0; i < CF::TN; ++i)
 #pragma unroll
-        for (int j = 0; j < CF::TM; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+        for (int f = 0; f < CF::TMF; ++f) acc[i][f] = v16i{};
 
-    v4i fa[2][CF::TM], fw[2][CF::TN];
-    auto read_frags = [&](int s, int j, int buf) {
+    v4i fa[2][CF::TMF], fw[2][CF::TN];
+    auto read_frags = [&](int s, int i, int buf) {
         const uint8_t* base = lds + (s % CF::NS) * CF::STAGE;
 #pragma unroll
-        for (int i = 0; i < CF::TM; ++i)
-            fa[buf][i] = operand_from_lds<ABITS, WBITS>(base + offa[j] + i * 16 * CF::RA);
+        for (int f = 0; f < CF::TMF; ++f)
+            fa[buf][f] = operand_from_lds<ABITS, WBITS>(base + offa[i] + f * 32 * CF::RA);
 #pragma unroll
-        for (int i = 0; i < CF::TN; ++i)
-            fw[buf][i] = operand_from_lds<WBITS, ABITS>(base + offw[j] + i * 16 * CF::RW);
+        for (int n = 0; n < CF::TN; ++n)
+            fw[buf][n] = operand_from_lds<WBITS, ABITS>(base + offw[i] + n * 32 * CF::RW);
     };
 
     // prologue: stages 0 .. NS-2 (clamped to the last stage when K is short)
@@ -239,25 +267,25 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
     read_frags(0, 0, 0);
 
     // this wave's loads of stage s + NS - 1 are spread over the MFMAs that follow
-    // the operand reads in steps 0 .. NSUB-2 (TM * (TN - 1) per step); whatever
+    // the operand reads in steps 0 .. NSTEP-2 (TMF * (TN - 1) per step); whatever
     // does not fit goes out at the start of the last step
-    constexpr int kSlotsPerStep = CF::TM * (CF::TN - 1);
-    constexpr int kDmaSlots = kSlotsPerStep * (CF::NSUB - 1);
+    constexpr int kSlotsPerStep = CF::TMF * (CF::TN - 1);
+    constexpr int kDmaSlots = kSlotsPerStep * (CF::NSTEP - 1);
     constexpr int kDmaEvery = kDmaSlots / CF::NHI > 0 ? kDmaSlots / CF::NHI : 1;
     constexpr int kDmaInLoop = kDmaSlots / kDmaEvery < CF::NHI ? kDmaSlots / kDmaEvery : CF::NHI;
 
-    // One k stage.  In each MFMA step the first TM MFMAs run on operands that
-    // were read one step earlier; then the next step's operands are read from
-    // LDS (their latency hides behind the remaining MFMAs).  Before the last
-    // step the next stage is waited for and published with the barrier.  A
-    // full stage has no data-dependent branches: past the end of K the refill
-    // loads re-read the last stage into the slot that was just freed (never
-    // read again), and the last stage reads operands once more without using
-    // them.  A half-deep last stage (FULL = false) runs its first NSUB/2 steps
-    // and neither loads nor waits.
+    // One k stage.  In each step the first TMF MFMAs run on operands read one
+    // step earlier; then the next step's operands are read from LDS (their
+    // latency hides behind the remaining MFMAs).  Before the last step the next
+    // stage is waited for and published with the barrier.  A full stage has no
+    // data-dependent branches: past the end of K the refill loads re-read the
+    // last stage into the slot that was just freed (never read again), and the
+    // last stage reads operands once more without using them.  A half-deep last
+    // stage (FULL = false) runs its first NSTEP/2 steps and neither loads nor
+    // waits.
     auto stage = [&](int s, auto full_tag) {
         constexpr bool kFull = decltype(full_tag)::value;
-        constexpr int kSteps = kFull ? CF::NSUB : CF::NSUB / 2;
+        constexpr int kSteps = kFull ? CF::NSTEP : CF::NSTEP / 2;
         const int refill = s + CF::NS - 1 < nk ? s + CF::NS - 1 : nk - 1;
         const int refill_slot = (s + CF::NS - 1) % CF::NS;
         const int next = s + 1 < nk ? s + 1 : nk - 1;
@@ -265,7 +293,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
         for (int j = 0; j < kSteps; ++j) {
             const int cur = j & 1;
 #pragma unroll
-            for (int ii = 0; ii < CF::TM; ++ii) acc[0][ii] = mfma16x16x64(fw[cur][0], fa[cur][ii], acc[0][ii]);
+            for (int f = 0; f < CF::TMF; ++f) acc[0][f] = mfma32x32x32(fw[cur][0], fa[cur][f], acc[0][f]);
             __builtin_amdgcn_sched_barrier(0);
             if (j + 1 < kSteps) {
                 read_frags(s, j + 1, cur ^ 1);
@@ -281,12 +309,12 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int i = 1; i < CF::TN; ++i)
+            for (int n = 1; n < CF::TN; ++n)
 #pragma unroll
-                for (int ii = 0; ii < CF::TM; ++ii) {
-                    acc[i][ii] = mfma16x16x64(fw[cur][i], fa[cur][ii], acc[i][ii]);
-                    if (kFull && j + 1 < CF::NSUB) {
-                        const int slot = j * kSlotsPerStep + (i - 1) * CF::TM + ii;
+                for (int f = 0; f < CF::TMF; ++f) {
+                    acc[n][f] = mfma32x32x32(fw[cur][n], fa[cur][f], acc[n][f]);
+                    if (kFull && j + 1 < CF::NSTEP) {
+                        const int slot = j * kSlotsPerStep + (n - 1) * CF::TMF + f;
                         if (slot % kDmaEvery == 0 && slot / kDmaEvery < kDmaInLoop) {
                             __builtin_amdgcn_sched_barrier(0);
                             dma(refill, refill_slot, slot / kDmaEvery);
@@ -300,20 +328,111 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
     const int nfull = nk - (half_last ? 1 : 0);
     for (int s = 0; s < nfull; ++s) stage(s, std::true_type{});
     if (half_last) stage(nk - 1, std::false_type{});
-    wait_vmcnt<0>();  // no load may still be writing LDS when the workgroup retires
 
-    // epilogue: lane holds D[n][m] for n = nb + 4 (lane / 16) + r, m = mb + lane % 16
+    // Split-k exchange through the (now idle) LDS ring: the k-half 0 wave of a
+    // pair keeps output fragments n < TN0, the k-half 1 wave the rest; each
+    // sends the other its partial sums of the fragments it does not keep.
+    wait_vmcnt<0>();  // every ring load has landed
+    barrier_nofence();  // and every wave is done reading the ring
+    {
+        uint8_t* xbase = lds + wm * (CF::TMF * CF::TN * 4096);
+#pragma unroll
+        for (int n = 0; n < CF::TN; ++n) {
+            if ((n < CF::TN0) == (kh == 0)) continue;  // kept by this wave
+#pragma unroll
+            for (int f = 0; f < CF::TMF; ++f)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const v4i v = {acc[n][f][4 * c], acc[n][f][4 * c + 1], acc[n][f][4 * c + 2], acc[n][f][4 * c + 3]};
+                    *reinterpret_cast<v4i*>(xbase + ((n * CF::TMF + f) * 4 + c) * 1024 + lane * 16) = v;
+                }
+        }
+        barrier_nofence();
+#pragma unroll
+        for (int n = 0; n < CF::TN; ++n) {
+            if ((n < CF::TN0) != (kh == 0)) continue;  // sent to the partner
+#pragma unroll
+            for (int f = 0; f < CF::TMF; ++f)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const v4i v = *reinterpret_cast<const v4i*>(xbase + ((n * CF::TMF + f) * 4 + c) * 1024 + lane * 16);
+                    acc[n][f][4 * c] += v[0];
+                    acc[n][f][4 * c + 1] += v[1];
+                    acc[n][f][4 * c + 2] += v[2];
+                    acc[n][f][4 * c + 3] += v[3];
+                }
+        }
+    }
+
+    // epilogue of the kept fragments: token m = m0 + wm BM/2 + 32 f + l % 32,
+    // rows n = n0 + 32 n + 8 q + 4 (l / 32) + i for register 4 q + i
+    constexpr int kKeep = CF::TN - CF::TN0 > CF::TN0 ? CF::TN - CF::TN0 : CF::TN0;
+    const int nfirst = kh == 0 ? 0 : CF::TN0;
+    const int nkeep = kh == 0 ? CF::TN0 : CF::TN - CF::TN0;
+    const int n_end = n0 + CF::BNS < g.N ? n0 + CF::BNS : g.N;
+    int mm[CF::TMF];
+    float sa[CF::TMF];
+#pragma unroll
+    for (int f = 0; f < CF::TMF; ++f) {
+        mm[f] = m0 + wm * (CF::BM / 2) + 32 * f + (lane & 31);
+        sa[f] = mm[f] < g.M ? g.act_scale[mm[f]] : 0.0f;
+    }
+    Out4 o[kKeep][4];
+    uint2 rs[kKeep][4][CF::TMF];
+#pragma unroll
+    for (int k = 0; k < kKeep; ++k)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int n = n0 + 32 * (nfirst + k) + 8 * q + 4 * (lane >> 5);
+            const bool ok = k < nkeep && n < n_end;
+            o[k][q].sw = ok ? *reinterpret_cast<const float4*>(g.wscale + n) : make_float4(0.f, 0.f, 0.f, 0.f);
+            o[k][q].bias = (ok && g.bias) ? *reinterpret_cast<const float4*>(g.bias + n) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int f = 0; f < CF::TMF; ++f)
+                rs[k][q][f] = (ok && g.residual && mm[f] < g.M)
+                                  ? *reinterpret_cast<const uint2*>(g.residual + int64_t(mm[f]) * g.ldr + n)
+                                  : make_uint2(0, 0);
+        }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no wait lands behind a store below
     constexpr int shift = AccShift<ABITS, WBITS>::value;
 #pragma unroll
-    for (int ii = 0; ii < CF::TM; ++ii) {
-        const int m = m0 + (wm * CF::TM + ii) * 16 + (lane & 15);
-        if (m >= g.M) continue;
-        const float sam = g.act_scale[m];
+    for (int k = 0; k < kKeep; ++k) {
+        if (k >= nkeep) continue;
+        // acc index nfirst + k, selected without dynamic register indexing
+        v16i a[CF::TMF];
 #pragma unroll
-        for (int i = 0; i < CF::TN; ++i) {
-            const int n = n0 + (wn * CF::TN + i) * 16 + (lane >> 4) * 4;
-            if (n >= g.N) continue;
-            store_out4(acc[i][ii], shift, m, n, sam, g.wscale, g.bias, g.residual, g.ldr, g.y, g.ldy, g.acc, g.N);
+        for (int f = 0; f < CF::TMF; ++f) a[f] = kh == 0 ? acc[k][f] : acc[(CF::TN0 + k) < CF::TN ? CF::TN0 + k : 0][f];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int n = n0 + 32 * (nfirst + k) + 8 * q + 4 * (lane >> 5);
+            if (n >= n_end) continue;
+#pragma unroll
+            for (int f = 0; f < CF::TMF; ++f) {
+                if (mm[f] >= g.M) continue;
+                const int a0 = a[f][4 * q] >> shift, a1 = a[f][4 * q + 1] >> shift;
+                const int a2 = a[f][4 * q + 2] >> shift, a3 = a[f][4 * q + 3] >> shift;
+                float t0 = float(a0) * (sa[f] * o[k][q].sw.x);
+                float t1 = float(a1) * (sa[f] * o[k][q].sw.y);
+                float t2 = float(a2) * (sa[f] * o[k][q].sw.z);
+                float t3 = float(a3) * (sa[f] * o[k][q].sw.w);
+                if (g.bias) {
+                    t0 = t0 + o[k][q].bias.x;
+                    t1 = t1 + o[k][q].bias.y;
+                    t2 = t2 + o[k][q].bias.z;
+                    t3 = t3 + o[k][q].bias.w;
+                }
+                if (g.residual) {
+                    t0 = t0 + bf16_lo(rs[k][q][f].x);
+                    t1 = t1 + bf16_hi(rs[k][q][f].x);
+                    t2 = t2 + bf16_lo(rs[k][q][f].y);
+                    t3 = t3 + bf16_hi(rs[k][q][f].y);
+                }
+                uint2 y;
+                y.x = f32_to_bf16(t0) | (f32_to_bf16(t1) << 16);
+                y.y = f32_to_bf16(t2) | (f32_to_bf16(t3) << 16);
+                *reinterpret_cast<uint2*>(g.y + int64_t(mm[f]) * g.ldy + n) = y;
+                if (g.acc) *reinterpret_cast<int4*>(g.acc + int64_t(mm[f]) * g.N + n) = make_int4(a0, a1, a2, a3);
+            }
         }
     }
 }
@@ -321,34 +440,49 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
 template <int ABITS, int WBITS, class CF>
 hipError_t launch_cfg(const GemmArgs& g, hipStream_t st) {
     const int tiles_m = (g.M + CF::BM - 1) / CF::BM;
-    const int tiles_n = (g.N + CF::BN - 1) / CF::BN;
+    const int tiles_n = (g.N + CF::BNS - 1) / CF::BNS;
     hipLaunchKernelGGL((gemm_kernel<ABITS, WBITS, CF>), dim3(tiles_m * tiles_n), dim3(kThreads), 0, st, g, tiles_m,
                        tiles_n);
     return hipGetLastError();
 }
 
-// Tile shapes (tokens x weight rows, wave grid, pipeline depth).
-enum TileId { T128x128 = 0, T128x144, T128x112, T256x128, T128x256, T64x128, kNumTiles };
+// Tile shapes: tokens x stored weight rows (computed rows rounded up to 32).
+enum TileId { T128x128 = 0, T128x144, T128x112, T128x96, T64x128, T64x224, T64x256, T64x288, kNumTiles };
 
-const char* const kTileNames[kNumTiles] = {"128x128", "128x144", "128x112", "256x128", "128x256", "64x128"};
+const char* const kTileNames[kNumTiles] = {"128x128", "128x144", "128x112", "128x96",
+                                           "64x128",  "64x224",  "64x256",  "64x288"};
+const int kTileBM[kNumTiles] = {128, 128, 128, 128, 64, 64, 64, 64};
+const int kTileBN[kNumTiles] = {128, 144, 112, 96, 128, 224, 256, 288};
 
-// Pipeline depth: as many stages as fit in 160 KiB of LDS, at most 5.
-template <int ABITS, int WBITS, int BM, int BN>
+// Pipeline depth: as many stages as fit in 160 KiB of LDS, at most 8.
+template <int ABITS, int WBITS, int BM, int BNC, int KS8 = 128>
 constexpr int ring_depth() {
-    constexpr int ks = (ABITS == 4 || WBITS == 4) ? 256 : 128;
-    constexpr int stage = (BM * ks * ABITS / 8) + (BN * ks * WBITS / 8);
+    constexpr int ks = (ABITS == 4 || WBITS == 4) ? 256 : KS8;
+    constexpr int stage = (BM * ks * ABITS / 8) + (BNC * ks * WBITS / 8);
     constexpr int n = 163840 / stage;
-    return n > 5 ? 5 : n;
+    return n > 8 ? 8 : n;
 }
 
-template <int ABITS, int WBITS, int BM, int BN, int WGM, int WGN>
+// Test hook: FQ_GEMM_KS=64 runs 8-bit x 8-bit GEMMs with 64-deep stages.
+int stage_override() {
+    const char* e = std::getenv("FQ_GEMM_KS");
+    return e ? std::atoi(e) : 0;
+}
+
+template <int ABITS, int WBITS, int BM, int BNS>
 hipError_t launch_shape(const GemmArgs& g, hipStream_t st) {
-    constexpr int ns = ring_depth<ABITS, WBITS, BM, BN>();
+    constexpr int bnc = (BNS + 31) / 32 * 32;
+    constexpr int ns = ring_depth<ABITS, WBITS, BM, bnc>();
+    if constexpr (ABITS == 8 && WBITS == 8) {
+        constexpr int ns64 = ring_depth<ABITS, WBITS, BM, bnc, 64>();
+        if (stage_override() == 64) return launch_cfg<ABITS, WBITS, Cfg<ABITS, WBITS, BM, BNS, bnc, ns64, 64>>(g, st);
+    }
     if constexpr (ns >= 3) {
-        return launch_cfg<ABITS, WBITS, Cfg<ABITS, WBITS, BM, BN, WGM, WGN, ns>>(g, st);
+        return launch_cfg<ABITS, WBITS, Cfg<ABITS, WBITS, BM, BNS, bnc, ns>>(g, st);
     } else {
         // this operand mix does not fit three stages of this tile: use 128 x 128
-        return launch_cfg<ABITS, WBITS, Cfg<ABITS, WBITS, 128, 128, 2, 2, ring_depth<ABITS, WBITS, 128, 128>()>>(g, st);
+        return launch_cfg<ABITS, WBITS, Cfg<ABITS, WBITS, 128, 128, 128, ring_depth<ABITS, WBITS, 128, 128>()>>(g,
+                                                                                                             st);
     }
 }
 
@@ -356,36 +490,38 @@ template <int ABITS, int WBITS>
 hipError_t launch_tile(int tile, const GemmArgs& g, hipStream_t st) {
     switch (tile) {
         case T128x144:
-            return launch_shape<ABITS, WBITS, 128, 144, 4, 1>(g, st);
+            return launch_shape<ABITS, WBITS, 128, 144>(g, st);
         case T128x112:
-            return launch_shape<ABITS, WBITS, 128, 112, 4, 1>(g, st);
-        case T256x128:
-            return launch_shape<ABITS, WBITS, 256, 128, 2, 2>(g, st);
-        case T128x256:
-            return launch_shape<ABITS, WBITS, 128, 256, 2, 2>(g, st);
+            return launch_shape<ABITS, WBITS, 128, 112>(g, st);
+        case T128x96:
+            return launch_shape<ABITS, WBITS, 128, 96>(g, st);
         case T64x128:
-            return launch_shape<ABITS, WBITS, 64, 128, 1, 4>(g, st);
+            return launch_shape<ABITS, WBITS, 64, 128>(g, st);
+        case T64x224:
+            return launch_shape<ABITS, WBITS, 64, 224>(g, st);
+        case T64x256:
+            return launch_shape<ABITS, WBITS, 64, 256>(g, st);
+        case T64x288:
+            return launch_shape<ABITS, WBITS, 64, 288>(g, st);
         case T128x128:
         default:
-            return launch_shape<ABITS, WBITS, 128, 128, 2, 2>(g, st);
+            return launch_shape<ABITS, WBITS, 128, 128>(g, st);
     }
 }
 
-// Pick the tile that minimises (waves of 256 workgroups) x (tile area): the
-// shapes of interest fill the 256 CUs in one wave with 128 x 144 (QKV, N = 4608)
-// or 128 x 112 (down projection, N = 3584).
+// Pick the tile that minimises (waves of 256 workgroups) x (computed tile area
+// / relative efficiency): 64-token tiles reuse each weight fragment half as
+// often.  The prefill shapes fill the 256 CUs in one wave with 128 x 144
+// (QKV, N = 4608) or 128 x 112 (down projection, N = 3584).
 int choose_tile(int M, int N) {
-    const int cand[] = {T128x128, T128x144, T128x112, T256x128, T128x256, T64x128};
-    const int bm[] = {128, 128, 128, 256, 128, 64};
-    const int bn[] = {128, 144, 112, 128, 256, 128};
-    // relative per-tile throughput (bigger tiles reuse operands better)
-    const double eff[] = {1.0, 1.03, 0.95, 1.15, 1.15, 0.8};
     int best = T128x128;
     double best_cost = 1e300;
-    for (int c : cand) {
-        const long tiles = long((M + bm[c] - 1) / bm[c]) * long((N + bn[c] - 1) / bn[c]);
+    for (int c = 0; c < kNumTiles; ++c) {
+        const int bm = kTileBM[c], bn = kTileBN[c], bnc = (bn + 31) / 32 * 32;
+        const long tiles = long((M + bm - 1) / bm) * long((N + bn - 1) / bn);
         const long waves = (tiles + 255) / 256;
-        const double cost = double(waves) * bm[c] * bn[c] / eff[c];
+        const double eff = bm == 128 ? 1.0 : 0.85;
+        const double cost = double(waves) * bm * bnc / eff;
         if (cost < best_cost * 0.999) {
             best_cost = cost;
             best = c;

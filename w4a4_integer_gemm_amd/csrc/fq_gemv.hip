@@ -146,17 +146,14 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(GemmArgs g, int pe
 
     // lane holds D[n = n0 + 16 r + 4 q + i][m = 16 t + lane % 16] of tile (r, t)
     constexpr int shift = AccShift<ABITS, WBITS>::value;
-    auto store = [&](const v4i a, int r, int t) {
-        const int n = n0 + 16 * r + q * 4;
-        const int m = t * 16 + (lane & 15);
-        if (n < g.N && m < g.M)
-            store_out4(a, shift, m, n, g.act_scale[m], g.wscale, g.bias, g.residual, g.ldr, g.y, g.ldy, g.acc, g.N);
-    };
     if (S == 1) {  // block-uniform
+        int mm[MT], nn[R];
 #pragma unroll
-        for (int r = 0; r < R; ++r)
+        for (int t = 0; t < MT; ++t) mm[t] = t * 16 + (lane & 15);
 #pragma unroll
-            for (int t = 0; t < MT; ++t) store(acc[r][t], r, t);
+        for (int r = 0; r < R; ++r) nn[r] = n0 + 16 * r + q * 4;
+        store_tiles<R, MT>(acc, shift, mm, nn, g.M, g.N, g.act_scale, g.wscale, g.bias, g.residual, g.ldr, g.y, g.ldy,
+                           g.acc);
         return;
     }
     // tile i = (r, t) = (i / MT, i % MT): wave i sums the S partials of tile i and stores it
@@ -166,9 +163,12 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(GemmArgs g, int pe
         for (int t = 0; t < MT; ++t) red[wave][r * MT + t][lane] = acc[r][t];
     __syncthreads();
     if (wave >= kTiles) return;
-    v4i sum = red[0][wave][lane];
-    for (int w = 1; w < S; ++w) sum += red[w][wave][lane];
-    store(sum, wave / MT, wave % MT);
+    v4i sum[1][1] = {{red[0][wave][lane]}};
+    for (int w = 1; w < S; ++w) sum[0][0] += red[w][wave][lane];
+    const int mm[1] = {(wave % MT) * 16 + (lane & 15)};
+    const int nn[1] = {n0 + 16 * (wave / MT) + q * 4};
+    store_tiles<1, 1>(sum, shift, mm, nn, g.M, g.N, g.act_scale, g.wscale, g.bias, g.residual, g.ldr, g.y, g.ldy,
+                      g.acc);
 }
 
 // Waves per workgroup: enough that a wave's share fits one batch of C units,
