@@ -41,7 +41,7 @@
 namespace fq {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;  // 4 MFMA waves + 4 load waves
 
 // 16-byte-per-lane global -> LDS copy (global_load_lds_dwordx4, SGPR base +
 // 32-bit VGPR offset form): lane l reads base + voff and its 16 bytes land at
@@ -153,18 +153,18 @@ __device__ __forceinline__ void slot_source(int q, int lane, int& rho, int& kc) 
     kc = (sigma % KC) ^ slot_swizzle<R>(rho);
 }
 
-// Epilogue of one 32 x 32 output fragment held by a wave (v_mfma_i32_32x32x32
-// layout: lane l holds token m, and rows n = 8 g + 4 (l / 32) + i of register
-// 4 g + i).  The caller has loaded every operand already (see store_tiles in
-// fq_device.h for why the loads come first).
-struct Out4 {
-    float4 sw, bias;
-    uint2 res;
-};
+// Row stride (int32 elements) of the accumulator tile staged in LDS for the
+// epilogue: BNC + 4 keeps a b128 write phase (16 consecutive tokens) on 16
+// distinct groups of four banks.
+template <class CF>
+constexpr int acc_stride() {
+    return CF::BNC + 4;
+}
 
 template <int ABITS, int WBITS, class CF>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m, int tiles_n) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[CF::LDS];
+    static_assert(CF::BM * acc_stride<CF>() * 4 <= CF::LDS, "the epilogue tile reuses the ring");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -186,252 +186,251 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
     // last stage may be half (128) deep
     const int nk = (g.K + CF::KS - 1) / CF::KS;
     const bool half_last = (g.K % CF::KS) != 0;
-
-    // This wave's load instructions: c = wave + 4 i.  Waves with one fewer
-    // instruction repeat their last one (same source, same LDS bytes), so every
-    // wave issues NHI loads per stage and the waits below are uniform.  Each
-    // load reads row-block base (scalar, advanced per stage) + a fixed per-lane
-    // offset.  In a half-deep last stage a lane whose column would run past the
-    // end of its row reads bytes of the stage's first 64 instead; that LDS slot
-    // is never used.
-    const uint8_t* abase = g.act + int64_t(m0) * lda;
-    const uint8_t* wbase = g.w + int64_t(n0) * ldw;
-    uint32_t voff[CF::NHI], dlast[CF::NHI];
-    int ldsoff[CF::NHI];
-    bool is_act[CF::NHI];
-#pragma unroll
-    for (int i = 0; i < CF::NHI; ++i) {
-        int c = wave + 4 * i;
-        if (c >= CF::C) c -= 4;
-        ldsoff[i] = c * 1024;
-        int rho, kc, rowoff, half;
-        is_act[i] = c < CF::CA;
-        if (c < CF::CA) {
-            slot_source<CF::RA>(c, lane, rho, kc);
-            int row = m0 + rho;
-            row = row < g.M ? row : g.M - 1;
-            rowoff = (row - m0) * int(lda);
-            half = CF::RA / 2;
-        } else {
-            slot_source<CF::RW>(c - CF::CA, lane, rho, kc);
-            int row = n0 + rho;
-            row = row < g.N ? row : g.N - 1;
-            rowoff = (row - n0) * int(ldw);
-            half = CF::RW / 2;
-        }
-        const int col = 16 * kc;
-        voff[i] = uint32_t(rowoff + col);
-        dlast[i] = uint32_t((col < half ? col : (col & 63)) - col);  // rows are at least 64 bytes
-    }
-    const uint32_t lds0 = lds_address(lds);
-    auto dma = [&](int stage_idx, int slot, int i) {
-        const uint8_t* base = is_act[i] ? abase + int64_t(stage_idx) * CF::RA : wbase + int64_t(stage_idx) * CF::RW;
-        const uint32_t off = voff[i] + ((half_last && stage_idx == nk - 1) ? dlast[i] : 0u);
-        copy16_to_lds(base, off, lds0 + uint32_t(slot * CF::STAGE + ldsoff[i]));
-    };
-
-    // wave roles: tokens wm * BM/2 .. + BM/2 (TMF fragments of 32), all BNC
-    // weight rows (TN fragments), and the MFMA k steps j = 2 i + kh of every stage
-    const int wm = wave & 1;
-    const int kh = wave >> 1;
-    int offa[CF::NSTEP], offw[CF::NSTEP];
-#pragma unroll
-    for (int i = 0; i < CF::NSTEP; ++i) {
-        offa[i] = operand_offset<ABITS, CF::RA>(lane, 2 * i + kh) + wm * CF::TMF * 32 * CF::RA;
-        offw[i] = operand_offset<WBITS, CF::RW>(lane, 2 * i + kh) + CF::CA * 1024;
-    }
-
-    v16i acc[CF::TN][CF::TMF];
-#pragma unroll
-    for (int i = 0; i < CF::TN; ++i)
-#pragma unroll
-        for (int f = 0; f < CF::TMF; ++f) acc[i][f] = v16i{};
-
-    v4i fa[2][CF::TMF], fw[2][CF::TN];
-    auto read_frags = [&](int s, int i, int buf) {
-        const uint8_t* base = lds + (s % CF::NS) * CF::STAGE;
-#pragma unroll
-        for (int f = 0; f < CF::TMF; ++f)
-            fa[buf][f] = operand_from_lds<ABITS, WBITS>(base + offa[i] + f * 32 * CF::RA);
-#pragma unroll
-        for (int n = 0; n < CF::TN; ++n)
-            fw[buf][n] = operand_from_lds<WBITS, ABITS>(base + offw[i] + n * 32 * CF::RW);
-    };
-
-    // prologue: stages 0 .. NS-2 (clamped to the last stage when K is short)
-    for (int s = 0; s < CF::NS - 1; ++s)
-#pragma unroll
-        for (int i = 0; i < CF::NHI; ++i) dma(s < nk ? s : nk - 1, s, i);
-    wait_vmcnt<(CF::NS - 2) * CF::NHI>();
-    barrier_nofence();
-    read_frags(0, 0, 0);
-
-    // this wave's loads of stage s + NS - 1 are spread over the MFMAs that follow
-    // the operand reads in steps 0 .. NSTEP-2 (TMF * (TN - 1) per step); whatever
-    // does not fit goes out at the start of the last step
-    constexpr int kSlotsPerStep = CF::TMF * (CF::TN - 1);
-    constexpr int kDmaSlots = kSlotsPerStep * (CF::NSTEP - 1);
-    constexpr int kDmaEvery = kDmaSlots / CF::NHI > 0 ? kDmaSlots / CF::NHI : 1;
-    constexpr int kDmaInLoop = kDmaSlots / kDmaEvery < CF::NHI ? kDmaSlots / kDmaEvery : CF::NHI;
-
-    // One k stage.  In each step the first TMF MFMAs run on operands read one
-    // step earlier; then the next step's operands are read from LDS (their
-    // latency hides behind the remaining MFMAs).  Before the last step the next
-    // stage is waited for and published with the barrier.  A full stage has no
-    // data-dependent branches: past the end of K the refill loads re-read the
-    // last stage into the slot that was just freed (never read again), and the
-    // last stage reads operands once more without using them.  A half-deep last
-    // stage (FULL = false) runs its first NSTEP/2 steps and neither loads nor
-    // waits.
-    auto stage = [&](int s, auto full_tag) {
-        constexpr bool kFull = decltype(full_tag)::value;
-        constexpr int kSteps = kFull ? CF::NSTEP : CF::NSTEP / 2;
-        const int refill = s + CF::NS - 1 < nk ? s + CF::NS - 1 : nk - 1;
-        const int refill_slot = (s + CF::NS - 1) % CF::NS;
-        const int next = s + 1 < nk ? s + 1 : nk - 1;
-#pragma unroll
-        for (int j = 0; j < kSteps; ++j) {
-            const int cur = j & 1;
-#pragma unroll
-            for (int f = 0; f < CF::TMF; ++f) acc[0][f] = mfma32x32x32(fw[cur][0], fa[cur][f], acc[0][f]);
-            __builtin_amdgcn_sched_barrier(0);
-            if (j + 1 < kSteps) {
-                read_frags(s, j + 1, cur ^ 1);
-            } else if (kFull) {
-#pragma unroll
-                for (int i = kDmaInLoop; i < CF::NHI; ++i) dma(refill, refill_slot, i);
-                // stage s+1 must have landed for every wave, and every wave must be
-                // done reading stage s-1's slot before anyone refills it
-                wait_vmcnt<(CF::NS - 2) * CF::NHI>();
-                __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-                barrier_nofence();
-                read_frags(next, 0, cur ^ 1);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int n = 1; n < CF::TN; ++n)
-#pragma unroll
-                for (int f = 0; f < CF::TMF; ++f) {
-                    acc[n][f] = mfma32x32x32(fw[cur][n], fa[cur][f], acc[n][f]);
-                    if (kFull && j + 1 < CF::NSTEP) {
-                        const int slot = j * kSlotsPerStep + (n - 1) * CF::TMF + f;
-                        if (slot % kDmaEvery == 0 && slot / kDmaEvery < kDmaInLoop) {
-                            __builtin_amdgcn_sched_barrier(0);
-                            dma(refill, refill_slot, slot / kDmaEvery);
-                            __builtin_amdgcn_sched_barrier(0);
-                        }
-                    }
-                }
-        }
-    };
-
     const int nfull = nk - (half_last ? 1 : 0);
-    for (int s = 0; s < nfull; ++s) stage(s, std::true_type{});
-    if (half_last) stage(nk - 1, std::false_type{});
 
-    // Split-k exchange through the (now idle) LDS ring: the k-half 0 wave of a
-    // pair keeps output fragments n < TN0, the k-half 1 wave the rest; each
-    // sends the other its partial sums of the fragments it does not keep.
-    wait_vmcnt<0>();  // every ring load has landed
-    barrier_nofence();  // and every wave is done reading the ring
-    {
-        uint8_t* xbase = lds + wm * (CF::TMF * CF::TN * 4096);
+    if (wave >= 4) {
+        // ---------------------------------------------------------- load waves
+        // Load wave p issues the stage's 1 KB copies c = p + 4 i; a wave with one
+        // fewer copy repeats its last one (same source, same LDS bytes), so all
+        // issue NHI per stage and the waits are uniform.  Each copy reads a
+        // row-block base (scalar, advanced per stage) + a fixed per-lane offset.
+        // In a half-deep last stage a lane whose column would run past the end
+        // of its row reads bytes of the stage's first 64 instead; that LDS slot
+        // is never read.
+        const int p = wave - 4;
+        const uint8_t* abase = g.act + int64_t(m0) * lda;
+        const uint8_t* wbase = g.w + int64_t(n0) * ldw;
+        uint32_t voff[CF::NHI], dlast[CF::NHI];
+        int ldsoff[CF::NHI];
+        bool is_act[CF::NHI];
 #pragma unroll
-        for (int n = 0; n < CF::TN; ++n) {
-            if ((n < CF::TN0) == (kh == 0)) continue;  // kept by this wave
-#pragma unroll
-            for (int f = 0; f < CF::TMF; ++f)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const v4i v = {acc[n][f][4 * c], acc[n][f][4 * c + 1], acc[n][f][4 * c + 2], acc[n][f][4 * c + 3]};
-                    *reinterpret_cast<v4i*>(xbase + ((n * CF::TMF + f) * 4 + c) * 1024 + lane * 16) = v;
-                }
+        for (int i = 0; i < CF::NHI; ++i) {
+            int c = p + 4 * i;
+            if (c >= CF::C) c -= 4;
+            ldsoff[i] = c * 1024;
+            int rho, kc, rowoff, half;
+            is_act[i] = c < CF::CA;
+            if (c < CF::CA) {
+                slot_source<CF::RA>(c, lane, rho, kc);
+                int row = m0 + rho;
+                row = row < g.M ? row : g.M - 1;
+                rowoff = (row - m0) * int(lda);
+                half = CF::RA / 2;
+            } else {
+                slot_source<CF::RW>(c - CF::CA, lane, rho, kc);
+                int row = n0 + rho;
+                row = row < g.N ? row : g.N - 1;
+                rowoff = (row - n0) * int(ldw);
+                half = CF::RW / 2;
+            }
+            const int col = 16 * kc;
+            voff[i] = uint32_t(rowoff + col);
+            dlast[i] = uint32_t((col < half ? col : (col & 63)) - col);  // rows are at least 64 bytes
         }
+        const uint32_t lds0 = lds_address(lds);
+        auto load_stage = [&](int stage_idx, int slot) {
+#pragma unroll
+            for (int i = 0; i < CF::NHI; ++i) {
+                const uint8_t* base =
+                    is_act[i] ? abase + int64_t(stage_idx) * CF::RA : wbase + int64_t(stage_idx) * CF::RW;
+                const uint32_t off = voff[i] + ((half_last && stage_idx == nk - 1) ? dlast[i] : 0u);
+                copy16_to_lds(base, off, lds0 + uint32_t(slot * CF::STAGE + ldsoff[i]));
+            }
+        };
+        // stages 0 .. NS-2 (clamped to the last stage when K is short), then
+        // publish stage 0
+        for (int s = 0; s < CF::NS - 1; ++s) load_stage(s < nk ? s : nk - 1, s);
+        wait_vmcnt<(CF::NS - 2) * CF::NHI>();
         barrier_nofence();
+        // After barrier s-1 every MFMA wave is done with stage s-1, whose slot
+        // takes stage s + NS - 1 (past the end of K: the last stage again, never
+        // read).  Barrier s publishes stage s + 1.
+        for (int s = 0; s < nfull; ++s) {
+            load_stage(s + CF::NS - 1 < nk ? s + CF::NS - 1 : nk - 1, (s + CF::NS - 1) % CF::NS);
+            wait_vmcnt<(CF::NS - 2) * CF::NHI>();
+            barrier_nofence();
+        }
+        wait_vmcnt<0>();      // every ring load has landed
+        barrier_nofence();    // E1: the ring is idle
+        barrier_nofence();    // E2: k-half 1 partial sums staged
+        barrier_nofence();    // E3: tile complete
+    } else {
+        // ---------------------------------------------------------- MFMA waves
+        // wave roles: tokens wm * BM/2 .. + BM/2 (TMF fragments of 32), all BNC
+        // weight rows (TN fragments), and the MFMA k steps j = 2 i + kh of every stage
+        const int wm = wave & 1;
+        const int kh = wave >> 1;
+        int offa[CF::NSTEP], offw[CF::NSTEP];
 #pragma unroll
-        for (int n = 0; n < CF::TN; ++n) {
-            if ((n < CF::TN0) != (kh == 0)) continue;  // sent to the partner
+        for (int i = 0; i < CF::NSTEP; ++i) {
+            offa[i] = operand_offset<ABITS, CF::RA>(lane, 2 * i + kh) + wm * CF::TMF * 32 * CF::RA;
+            offw[i] = operand_offset<WBITS, CF::RW>(lane, 2 * i + kh) + CF::CA * 1024;
+        }
+
+        v16i acc[CF::TN][CF::TMF];
+#pragma unroll
+        for (int i = 0; i < CF::TN; ++i)
+#pragma unroll
+            for (int f = 0; f < CF::TMF; ++f) acc[i][f] = v16i{};
+
+        v4i fa[2][CF::TMF], fw[2][CF::TN];
+        auto read_frags = [&](int s, int i, int buf) {
+            const uint8_t* base = lds + (s % CF::NS) * CF::STAGE;
 #pragma unroll
             for (int f = 0; f < CF::TMF; ++f)
+                fa[buf][f] = operand_from_lds<ABITS, WBITS>(base + offa[i] + f * 32 * CF::RA);
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const v4i v = *reinterpret_cast<const v4i*>(xbase + ((n * CF::TMF + f) * 4 + c) * 1024 + lane * 16);
-                    acc[n][f][4 * c] += v[0];
-                    acc[n][f][4 * c + 1] += v[1];
-                    acc[n][f][4 * c + 2] += v[2];
-                    acc[n][f][4 * c + 3] += v[3];
+            for (int n = 0; n < CF::TN; ++n)
+                fw[buf][n] = operand_from_lds<WBITS, ABITS>(base + offw[i] + n * 32 * CF::RW);
+        };
+
+        barrier_nofence();  // stage 0 published
+        read_frags(0, 0, 0);
+
+        // One k stage.  In each step the first TMF MFMAs run on operands read
+        // one step earlier; then the next step's operands are read from LDS
+        // (their latency hides behind the remaining MFMAs).  Before the last
+        // step this wave's reads of the stage are waited for and the barrier
+        // both frees the stage's slot and publishes the next stage.  A
+        // half-deep last stage (FULL = false) runs its first NSTEP/2 steps and
+        // has no barrier.
+        auto stage = [&](int s, auto full_tag) {
+            constexpr bool kFull = decltype(full_tag)::value;
+            constexpr int kSteps = kFull ? CF::NSTEP : CF::NSTEP / 2;
+            const int next = s + 1 < nk ? s + 1 : nk - 1;
+#pragma unroll
+            for (int j = 0; j < kSteps; ++j) {
+                const int cur = j & 1;
+#pragma unroll
+                for (int f = 0; f < CF::TMF; ++f) acc[0][f] = mfma32x32x32(fw[cur][0], fa[cur][f], acc[0][f]);
+                __builtin_amdgcn_sched_barrier(0);
+                if (j + 1 < kSteps) {
+                    read_frags(s, j + 1, cur ^ 1);
+                } else if (kFull) {
+                    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+                    barrier_nofence();
+                    read_frags(next, 0, cur ^ 1);
                 }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int n = 1; n < CF::TN; ++n)
+#pragma unroll
+                    for (int f = 0; f < CF::TMF; ++f) acc[n][f] = mfma32x32x32(fw[cur][n], fa[cur][f], acc[n][f]);
+            }
+        };
+        for (int s = 0; s < nfull; ++s) stage(s, std::true_type{});
+        if (half_last) stage(nk - 1, std::false_type{});
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's ring reads are done
+        barrier_nofence();                   // E1: the ring is idle
+
+        // Stage the accumulator tile X[BM][BNC] (int32, row stride XS) in the
+        // ring: the k-half 1 waves write their partial sums, then the k-half 0
+        // waves add theirs.  Lane l holds token wm BM/2 + 32 f + l % 32 and rows
+        // 32 n + 8 q + 4 (l / 32) + [0, 4) of fragment (n, f) in registers 4 q ...
+        int32_t* X = reinterpret_cast<int32_t*>(lds);
+        constexpr int XS = acc_stride<CF>();
+        auto xrow = [&](int f, int n, int q) {
+            const int m = wm * (CF::BM / 2) + 32 * f + (lane & 31);
+            return reinterpret_cast<v4i*>(X + m * XS + 32 * n + 8 * q + 4 * (lane >> 5));
+        };
+        if (kh == 1) {
+#pragma unroll
+            for (int n = 0; n < CF::TN; ++n)
+#pragma unroll
+                for (int f = 0; f < CF::TMF; ++f)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        *xrow(f, n, q) = v4i{acc[n][f][4 * q], acc[n][f][4 * q + 1], acc[n][f][4 * q + 2],
+                                             acc[n][f][4 * q + 3]};
         }
+        barrier_nofence();  // E2
+        if (kh == 0) {
+#pragma unroll
+            for (int n = 0; n < CF::TN; ++n)
+#pragma unroll
+                for (int f = 0; f < CF::TMF; ++f)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        v4i* p = xrow(f, n, q);
+                        const v4i v = *p;
+                        *p = v4i{acc[n][f][4 * q] + v[0], acc[n][f][4 * q + 1] + v[1], acc[n][f][4 * q + 2] + v[2],
+                                 acc[n][f][4 * q + 3] + v[3]};
+                    }
+        }
+        barrier_nofence();  // E3
     }
 
-    // epilogue of the kept fragments: token m = m0 + wm BM/2 + 32 f + l % 32,
-    // rows n = n0 + 32 n + 8 q + 4 (l / 32) + i for register 4 q + i
-    constexpr int kKeep = CF::TN - CF::TN0 > CF::TN0 ? CF::TN - CF::TN0 : CF::TN0;
-    const int nfirst = kh == 0 ? 0 : CF::TN0;
-    const int nkeep = kh == 0 ? CF::TN0 : CF::TN - CF::TN0;
-    const int n_end = n0 + CF::BNS < g.N ? n0 + CF::BNS : g.N;
-    int mm[CF::TMF];
-    float sa[CF::TMF];
-#pragma unroll
-    for (int f = 0; f < CF::TMF; ++f) {
-        mm[f] = m0 + wm * (CF::BM / 2) + 32 * f + (lane & 31);
-        sa[f] = mm[f] < g.M ? g.act_scale[mm[f]] : 0.0f;
-    }
-    Out4 o[kKeep][4];
-    uint2 rs[kKeep][4][CF::TMF];
-#pragma unroll
-    for (int k = 0; k < kKeep; ++k)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int n = n0 + 32 * (nfirst + k) + 8 * q + 4 * (lane >> 5);
-            const bool ok = k < nkeep && n < n_end;
-            o[k][q].sw = ok ? *reinterpret_cast<const float4*>(g.wscale + n) : make_float4(0.f, 0.f, 0.f, 0.f);
-            o[k][q].bias = (ok && g.bias) ? *reinterpret_cast<const float4*>(g.bias + n) : make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-            for (int f = 0; f < CF::TMF; ++f)
-                rs[k][q][f] = (ok && g.residual && mm[f] < g.M)
-                                  ? *reinterpret_cast<const uint2*>(g.residual + int64_t(mm[f]) * g.ldr + n)
-                                  : make_uint2(0, 0);
+    // ---------------------------------------------------------------- epilogue
+    // All eight waves: wave w takes tile rows w BM/8 .. + BM/8; a lane takes 8
+    // consecutive outputs n .. n + 7 of one token (one 16-byte bf16 store):
+    //   y[m][n] = bf16_rne(float(acc >> shift) * (s_m * s_n) [+ bias_n] [+ residual_mn])
+    // in float32, one rounding per step.  Every operand is loaded before the
+    // first store (a load queued behind a store would wait for it).
+    {
+        const int32_t* X = reinterpret_cast<const int32_t*>(lds);
+        constexpr int XS = acc_stride<CF>();
+        constexpr int LPR = CF::BNS / 8;   // lanes per token row
+        constexpr int RPI = 64 / LPR;      // token rows per pass
+        constexpr int ROWS = CF::BM / 8;   // token rows per wave
+        constexpr int NIT = (ROWS + RPI - 1) / RPI;
+        constexpr int shift = AccShift<ABITS, WBITS>::value;
+        const int lr = lane / LPR, lc = lane % LPR;
+        const int n = n0 + 8 * lc;
+        const bool col_ok = lr < RPI && n < g.N;
+        float4 sw0 = make_float4(0.f, 0.f, 0.f, 0.f), sw1 = sw0, b0 = sw0, b1 = sw0;
+        if (col_ok) {
+            sw0 = *reinterpret_cast<const float4*>(g.wscale + n);
+            sw1 = *reinterpret_cast<const float4*>(g.wscale + n + 4);
+            if (g.bias) {
+                b0 = *reinterpret_cast<const float4*>(g.bias + n);
+                b1 = *reinterpret_cast<const float4*>(g.bias + n + 4);
+            }
         }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no wait lands behind a store below
-    constexpr int shift = AccShift<ABITS, WBITS>::value;
+        bool ok[NIT];
+        int rr[NIT];
+        float sa[NIT];
+        uint4 rs[NIT];
 #pragma unroll
-    for (int k = 0; k < kKeep; ++k) {
-        if (k >= nkeep) continue;
-        // acc index nfirst + k, selected without dynamic register indexing
-        v16i a[CF::TMF];
+        for (int it = 0; it < NIT; ++it) {
+            rr[it] = wave * ROWS + it * RPI + lr;
+            const int m = m0 + rr[it];
+            ok[it] = col_ok && it * RPI + lr < ROWS && m < g.M;
+            sa[it] = ok[it] ? g.act_scale[m] : 0.0f;
+            rs[it] = (ok[it] && g.residual) ? *reinterpret_cast<const uint4*>(g.residual + int64_t(m) * g.ldr + n)
+                                            : make_uint4(0, 0, 0, 0);
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 #pragma unroll
-        for (int f = 0; f < CF::TMF; ++f) a[f] = kh == 0 ? acc[k][f] : acc[(CF::TN0 + k) < CF::TN ? CF::TN0 + k : 0][f];
+        for (int it = 0; it < NIT; ++it) {
+            if (!ok[it]) continue;
+            const int m = m0 + rr[it];
+            const v4i x0 = *reinterpret_cast<const v4i*>(X + rr[it] * XS + 8 * lc);
+            const v4i x1 = *reinterpret_cast<const v4i*>(X + rr[it] * XS + 8 * lc + 4);
+            const int a[8] = {x0[0] >> shift, x0[1] >> shift, x0[2] >> shift, x0[3] >> shift,
+                              x1[0] >> shift, x1[1] >> shift, x1[2] >> shift, x1[3] >> shift};
+            const float sw[8] = {sw0.x, sw0.y, sw0.z, sw0.w, sw1.x, sw1.y, sw1.z, sw1.w};
+            const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+            const uint32_t rw[4] = {rs[it].x, rs[it].y, rs[it].z, rs[it].w};
+            uint32_t o[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int n = n0 + 32 * (nfirst + k) + 8 * q + 4 * (lane >> 5);
-            if (n >= n_end) continue;
-#pragma unroll
-            for (int f = 0; f < CF::TMF; ++f) {
-                if (mm[f] >= g.M) continue;
-                const int a0 = a[f][4 * q] >> shift, a1 = a[f][4 * q + 1] >> shift;
-                const int a2 = a[f][4 * q + 2] >> shift, a3 = a[f][4 * q + 3] >> shift;
-                float t0 = float(a0) * (sa[f] * o[k][q].sw.x);
-                float t1 = float(a1) * (sa[f] * o[k][q].sw.y);
-                float t2 = float(a2) * (sa[f] * o[k][q].sw.z);
-                float t3 = float(a3) * (sa[f] * o[k][q].sw.w);
+            for (int e = 0; e < 8; e += 2) {
+                float t0 = float(a[e]) * (sa[it] * sw[e]);
+                float t1 = float(a[e + 1]) * (sa[it] * sw[e + 1]);
                 if (g.bias) {
-                    t0 = t0 + o[k][q].bias.x;
-                    t1 = t1 + o[k][q].bias.y;
-                    t2 = t2 + o[k][q].bias.z;
-                    t3 = t3 + o[k][q].bias.w;
+                    t0 = t0 + bb[e];
+                    t1 = t1 + bb[e + 1];
                 }
                 if (g.residual) {
-                    t0 = t0 + bf16_lo(rs[k][q][f].x);
-                    t1 = t1 + bf16_hi(rs[k][q][f].x);
-                    t2 = t2 + bf16_lo(rs[k][q][f].y);
-                    t3 = t3 + bf16_hi(rs[k][q][f].y);
+                    t0 = t0 + bf16_lo(rw[e / 2]);
+                    t1 = t1 + bf16_hi(rw[e / 2]);
                 }
-                uint2 y;
-                y.x = f32_to_bf16(t0) | (f32_to_bf16(t1) << 16);
-                y.y = f32_to_bf16(t2) | (f32_to_bf16(t3) << 16);
-                *reinterpret_cast<uint2*>(g.y + int64_t(mm[f]) * g.ldy + n) = y;
-                if (g.acc) *reinterpret_cast<int4*>(g.acc + int64_t(mm[f]) * g.N + n) = make_int4(a0, a1, a2, a3);
+                o[e / 2] = f32_to_bf16(t0) | (f32_to_bf16(t1) << 16);
+            }
+            *reinterpret_cast<uint4*>(g.y + int64_t(m) * g.ldy + n) = make_uint4(o[0], o[1], o[2], o[3]);
+            if (g.acc) {
+                int32_t* ap = g.acc + int64_t(m) * g.N + n;
+                *reinterpret_cast<int4*>(ap) = make_int4(a[0], a[1], a[2], a[3]);
+                *reinterpret_cast<int4*>(ap + 4) = make_int4(a[4], a[5], a[6], a[7]);
             }
         }
     }
