@@ -102,6 +102,23 @@ fq_status fq_pack_weights(const float* W, int32_t N, int32_t K, const float* asc
                           int32_t fold_after, int32_t hblock, int32_t wbits,
                           void* codes_out, float* wscale_out);
 
+/* Dequantised float weight rows in the original frame: the page's dequant mode,
+ * which rebuilds every site as a float GEMM weight for backends without the
+ * integer nodes (dequant-mode commit: row n of the float weight is R(w_n)/a or
+ * R(w_n/a)).  With v = wscale[n] * q_n (the stored codes):
+ *   fold_after 0: W_out[n] = R_b(v) / a      fold_after 1: W_out[n] = R_b(v / a)
+ * which undoes fq_pack_weights' fold exactly (R_b is its own inverse), leaving
+ * only the rounding of the codes.  ascale NULL means a = 1; at norm sites the
+ * smoothing vector lives in the folded gain, so there the float path uses the
+ * folded gain with these rows.
+ *   codes, wscale  host, as written by fq_pack_weights (same N, K, hblock, wbits)
+ *   W_out          host float32 [N][K]
+ * Float64 inside, one rounding to float32.  Same argument rules as
+ * fq_pack_weights; wscale must be finite and >= 0. */
+fq_status fq_dequant_rows(const void* codes, const float* wscale, int32_t N, int32_t K,
+                          const float* ascale, int32_t fold_after, int32_t hblock, int32_t wbits,
+                          float* W_out);
+
 /* ------------------------------------------------------------------ device, asynchronous */
 
 /* Prologue: quantise M bf16 tokens into codes and per-token scales.

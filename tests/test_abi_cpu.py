@@ -77,6 +77,69 @@ def test_host_packer_matches_oracle_on_workload_shapes():
     assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
 
 
+def _ulp_diff(a32, b32):
+    """Distance in float32 units in the last place (same sign assumed near equality)."""
+    ai = a32.view(np.int32).astype(np.int64)
+    bi = b32.view(np.int32).astype(np.int64)
+    ai = np.where(ai < 0, -(ai & 0x7FFFFFFF), ai)
+    bi = np.where(bi < 0, -(bi & 0x7FFFFFFF), bi)
+    return np.abs(ai - bi)
+
+
+@pytest.mark.parametrize("wbits", [8, 4])
+@pytest.mark.parametrize("fold_after", [0, 1])
+@pytest.mark.parametrize("hblock", [1, 16, 128])
+@pytest.mark.parametrize("with_a", [False, True])
+def test_dequant_rows_match_oracle_unfold(wbits, fold_after, hblock, with_a):
+    """fq_dequant_rows against the oracle's float64 unfold, rounded once to
+    float32: equal to within one float32 unit in the last place (the two sum
+    the butterfly in different orders)."""
+    rng = np.random.default_rng(hblock + 3 * wbits + fold_after)
+    N, K = 20, 384
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    a = rng.uniform(0.2, 5.0, K).astype(np.float32) if with_a else None
+    codes, ws = oracle.pack_weights(W, a, fold_after, hblock, wbits)
+    got = fq.fq_dequant_rows(codes, ws, K, a, fold_after, hblock, wbits)
+    ref = oracle.unfold_weights(codes, ws, K, a, fold_after, hblock, wbits).astype(np.float32)
+    d = _ulp_diff(got, ref)
+    small = np.abs(ref) < 1e-30
+    assert np.all(d[~small] <= 1), f"max ulp diff {d[~small].max()}"
+    assert np.all(np.abs(got[small]) < 1e-29)
+
+
+@pytest.mark.parametrize("wbits", [8, 4])
+@pytest.mark.parametrize("fold_after", [0, 1])
+def test_dequant_rows_undo_the_fold_up_to_rounding(wbits, fold_after):
+    """The rebuild returns the original rows up to the codes' rounding: per row,
+    in the smoothing-weighted norm the fold preserves, the error is at most
+    half a quantisation step per element (sqrt(K) s_n / 2)."""
+    rng = np.random.default_rng(11 + wbits + fold_after)
+    N, K, b = 16, 512, 64
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    a = rng.uniform(0.3, 3.0, K).astype(np.float32)
+    codes, ws = fq.fq_pack_weights(W, a, fold_after, b, wbits)
+    back = fq.fq_dequant_rows(codes, ws, K, a, fold_after, b, wbits).astype(np.float64)
+    err = back - W.astype(np.float64)
+    for n in range(N):
+        bound = np.sqrt(K) * ws[n] / 2 * (1 + 1e-6)
+        weighted = err[n] * a if fold_after == 0 else err[n]
+        scale = 1.0 if fold_after == 0 else 1.0 / a.min()
+        assert np.linalg.norm(weighted) <= bound * scale + 1e-12
+
+
+def test_dequant_rows_rejects():
+    codes = np.zeros((4, 256), np.uint8)
+    ws = np.ones(4, np.float32)
+    with pytest.raises(fq.FqError, match="fq_dequant_rows: K=100"):
+        fq.fq_dequant_rows(codes, ws, 100, None, 0, 1, 8)
+    with pytest.raises(fq.FqError, match="fq_dequant_rows: K=256 not divisible by hblock=512|hblock=512"):
+        fq.fq_dequant_rows(codes, ws, 256, None, 0, 512, 8)
+    bad = ws.copy()
+    bad[2] = np.nan
+    with pytest.raises(fq.FqError, match=r"wscale\[2\]"):
+        fq.fq_dequant_rows(codes, bad, 256, None, 0, 1, 8)
+
+
 def test_fold_gain_matches_oracle():
     rng = np.random.default_rng(1)
     g = rng.uniform(0.5, 1.5, 3584).astype(np.float32)

@@ -85,3 +85,24 @@ def test_linear_workload_full_size_sampled(name):
     rows = np.unique(np.concatenate([[0, wl.M - 1], rng.choice(wl.M, size=min(wl.M, 24), replace=False)]))
     log(f"linear workload {name}: M={wl.M} K={wl.K} N={wl.N} rows checked {len(rows)}")
     check_linear(wl, site, rows=rows, what=name)
+
+
+@pytest.mark.parametrize("name,max_rel", [("qkv_w8a8", 0.03), ("gateup_w4a4", 0.35)])
+def test_dequant_float_path_agrees_with_integer_path(name, max_rel):
+    """The page's dequant mode: a float GEMM on the un-rotated activations with the
+    rows fq_dequant_rows rebuilds (the smoothing vector stays in the folded norm
+    gain) computes the same layer as the integer path, up to the activations'
+    quantisation (8-bit: ~1 %, 4-bit: 15 levels)."""
+    wl = synth.make_workload(name, M=64, N=512)
+    site = site_for(wl)
+    y = host(site.linear(dev(wl.x)), np.uint16)
+    y_int = synth.bf16_bits_to_f32(y).astype(np.float64)
+    gamma_f = oracle.fold_gain(wl.gamma, wl.ascale).astype(np.float64)
+    x = synth.bf16_bits_to_f32(wl.x).astype(np.float64)
+    xn = x / np.sqrt(np.mean(x * x, axis=1, keepdims=True) + wl.eps) * gamma_f
+    W_deq = fq.fq_dequant_rows(site.codes_host, site.wscale_host, wl.K, None, 0, wl.hblock, wl.wbits)
+    y_float = xn @ W_deq.astype(np.float64).T
+    rel = np.linalg.norm(y_int - y_float) / np.linalg.norm(y_float)
+    cos = float(np.sum(y_int * y_float) / (np.linalg.norm(y_int) * np.linalg.norm(y_float)))
+    log(f"dequant vs integer {name}: rel {rel:.3e} cosine {cos:.6f}")
+    assert rel <= max_rel and cos >= 1 - max_rel ** 2

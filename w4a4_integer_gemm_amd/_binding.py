@@ -29,6 +29,7 @@ SIGNATURES = {
     "fq_act_bytes": ([_I32, _I32, _I32], _SZ),
     "fq_fold_gain": ([_P, _P, _I32, _P], ctypes.c_int),
     "fq_pack_weights": ([_P, _I32, _I32, _P, _I32, _I32, _I32, _P, _P], ctypes.c_int),
+    "fq_dequant_rows": ([_P, _P, _I32, _I32, _P, _I32, _I32, _I32, _P], ctypes.c_int),
     "fq_prologue": ([_P, _I32, _I32, _I64, _P, _F, _P, _I32, _I32, _I32, _P, _P, _P], ctypes.c_int),
     "fq_gemm": ([_P, _P, _I32, _I32, _P, _P, _I32, _I32, _I32, _P, _P, _I64, _P, _I64, _P, _P], ctypes.c_int),
     "fq_linear_workspace_bytes": ([_I32, _I32, _I32], _SZ),
@@ -114,6 +115,19 @@ def fq_pack_weights(W: np.ndarray, ascale: Optional[np.ndarray], fold_after: int
     _check(lib().fq_pack_weights(_np_ptr(W), N, K, _np_ptr(a), fold_after, hblock, wbits, _np_ptr(codes),
                                  _np_ptr(ws)))
     return codes, ws
+
+
+def fq_dequant_rows(codes: np.ndarray, wscale: np.ndarray, K: int, ascale: Optional[np.ndarray], fold_after: int,
+                    hblock: int, wbits: int) -> np.ndarray:
+    """Host dequantisation to float rows in the original frame; returns float32 [N][K]."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    ws = np.ascontiguousarray(wscale, dtype=np.float32)
+    N = ws.shape[0]
+    a = None if ascale is None else np.ascontiguousarray(ascale, dtype=np.float32)
+    out = np.empty((N, K), np.float32)
+    _check(lib().fq_dequant_rows(_np_ptr(codes), _np_ptr(ws), N, K, _np_ptr(a), fold_after, hblock, wbits,
+                                 _np_ptr(out)))
+    return out
 
 
 # ------------------------------------------------------------------ device entry points

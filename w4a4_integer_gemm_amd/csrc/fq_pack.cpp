@@ -75,6 +75,93 @@ void pack_rows(const float* W, int32_t n0, int32_t n1, int32_t K, const float* a
     }
 }
 
+// Dequantised row in the original frame: v = s q, then R(v)/a (fold before) or
+// R(v/a) (fold after); R is its own inverse, so this undoes the packer's fold.
+void dequant_rows(const uint8_t* codes, const float* wscale, int32_t n0, int32_t n1, int32_t K, const float* a,
+                  int32_t fold_after, int32_t b, int32_t bits, float* W) {
+    const size_t row_bytes = bits == 8 ? size_t(K) : size_t(K / 2);
+    std::vector<double> v(K);
+    for (int32_t n = n0; n < n1; ++n) {
+        const uint8_t* row = codes + size_t(n) * row_bytes;
+        const double s = static_cast<double>(wscale[n]);
+        for (int32_t k = 0; k < K; ++k) {
+            int32_t q;
+            if (bits == 8) {
+                q = static_cast<int8_t>(row[k]);
+            } else {
+                const int32_t nib = (row[k / 2] >> (4 * (k & 1))) & 0xF;
+                q = nib >= 8 ? nib - 16 : nib;
+            }
+            v[k] = s * static_cast<double>(q);
+        }
+        if (a && fold_after)
+            for (int32_t k = 0; k < K; ++k) v[k] /= static_cast<double>(a[k]);
+        rotate_row(v.data(), K, b);
+        if (a && !fold_after)
+            for (int32_t k = 0; k < K; ++k) v[k] /= static_cast<double>(a[k]);
+        float* w = W + int64_t(n) * K;
+        for (int32_t k = 0; k < K; ++k) w[k] = static_cast<float>(v[k]);
+    }
+}
+
+// Shared argument checks of the two host row transforms; returns FQ_OK or sets the message.
+fq_status check_rows(const char* fn, int32_t N, int32_t K, const float* ascale, int32_t fold_after, int32_t hblock,
+                     int32_t wbits) {
+    char buf[256];
+    auto fail = [&](fq_status s) {
+        fq::set_error(buf);
+        return s;
+    };
+    if (wbits != 8 && wbits != 4) {
+        snprintf(buf, sizeof buf, "%s: wbits=%d is not a supported code width (4 or 8)", fn, wbits);
+        return fail(FQ_ERR_UNSUPPORTED);
+    }
+    if (N < 1) {
+        snprintf(buf, sizeof buf, "%s: N=%d must be >= 1", fn, N);
+        return fail(FQ_ERR_SHAPE);
+    }
+    if (K < 128 || K > 65536 || K % 128) {
+        snprintf(buf, sizeof buf, "%s: K=%d must be a multiple of 128 in [128, 65536] (%d/128 = %.2f)", fn, K, K,
+                 K / 128.0);
+        return fail(FQ_ERR_SHAPE);
+    }
+    if (hblock < 1 || hblock > 256 || (hblock & (hblock - 1))) {
+        snprintf(buf, sizeof buf, "%s: hblock=%d must be a power of two in [1, 256]", fn, hblock);
+        return fail(FQ_ERR_SHAPE);
+    }
+    if (K % hblock) {
+        snprintf(buf, sizeof buf, "%s: K=%d not divisible by hblock=%d (%d/%d = %.2f)", fn, K, hblock, K, hblock,
+                 double(K) / hblock);
+        return fail(FQ_ERR_SHAPE);
+    }
+    if (fold_after != 0 && fold_after != 1) {
+        snprintf(buf, sizeof buf, "%s: fold_after=%d must be 0 or 1", fn, fold_after);
+        return fail(FQ_ERR_ARG);
+    }
+    if (ascale)
+        for (int32_t k = 0; k < K; ++k)
+            if (!(ascale[k] > 0.0f) || !std::isfinite(ascale[k])) {
+                snprintf(buf, sizeof buf, "%s: ascale[%d]=%g must be finite and > 0", fn, k, double(ascale[k]));
+                return fail(FQ_ERR_ARG);
+            }
+    return FQ_OK;
+}
+
+// Runs rows [0, N) of `fn(n0, n1)` on up to 16 host threads.
+template <class F>
+void parallel_rows(int32_t N, F fn) {
+    unsigned nt = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
+    nt = std::min<unsigned>(nt, unsigned(N));
+    std::vector<std::thread> pool;
+    const int32_t per = (N + int32_t(nt) - 1) / int32_t(nt);
+    for (unsigned t = 0; t < nt; ++t) {
+        const int32_t n0 = int32_t(t) * per, n1 = std::min(N, n0 + per);
+        if (n0 >= n1) break;
+        pool.emplace_back(fn, n0, n1);
+    }
+    for (auto& th : pool) th.join();
+}
+
 }  // namespace
 
 extern "C" fq_status fq_pack_weights(const float* W, int32_t N, int32_t K, const float* ascale, int32_t fold_after,
@@ -85,50 +172,33 @@ extern "C" fq_status fq_pack_weights(const float* W, int32_t N, int32_t K, const
         return s;
     };
     if (!W || !codes_out || !wscale_out) return fail(FQ_ERR_ARG, "fq_pack_weights: W, codes_out or wscale_out is NULL");
-    char buf[256];
-    if (wbits != 8 && wbits != 4) {
-        snprintf(buf, sizeof buf, "fq_pack_weights: wbits=%d is not a supported code width (4 or 8)", wbits);
-        return fail(FQ_ERR_UNSUPPORTED, buf);
+    const fq_status st = check_rows("fq_pack_weights", N, K, ascale, fold_after, hblock, wbits);
+    if (st != FQ_OK) return st;
+    parallel_rows(N, [&](int32_t n0, int32_t n1) {
+        pack_rows(W, n0, n1, K, ascale, fold_after, hblock, wbits, static_cast<uint8_t*>(codes_out), wscale_out);
+    });
+    return FQ_OK;
+}
+
+extern "C" fq_status fq_dequant_rows(const void* codes, const float* wscale, int32_t N, int32_t K,
+                                     const float* ascale, int32_t fold_after, int32_t hblock, int32_t wbits,
+                                     float* W_out) {
+    fq::clear_error();
+    if (!codes || !wscale || !W_out) {
+        fq::set_error("fq_dequant_rows: codes, wscale or W_out is NULL");
+        return FQ_ERR_ARG;
     }
-    if (N < 1) {
-        snprintf(buf, sizeof buf, "fq_pack_weights: N=%d must be >= 1", N);
-        return fail(FQ_ERR_SHAPE, buf);
-    }
-    if (K < 128 || K > 65536 || K % 128) {
-        snprintf(buf, sizeof buf, "fq_pack_weights: K=%d must be a multiple of 128 in [128, 65536] (%d/128 = %.2f)",
-                 K, K, K / 128.0);
-        return fail(FQ_ERR_SHAPE, buf);
-    }
-    if (hblock < 1 || hblock > 256 || (hblock & (hblock - 1))) {
-        snprintf(buf, sizeof buf, "fq_pack_weights: hblock=%d must be a power of two in [1, 256]", hblock);
-        return fail(FQ_ERR_SHAPE, buf);
-    }
-    if (K % hblock) {
-        snprintf(buf, sizeof buf, "fq_pack_weights: K=%d not divisible by hblock=%d (%d/%d = %.2f)", K, hblock, K,
-                 hblock, double(K) / hblock);
-        return fail(FQ_ERR_SHAPE, buf);
-    }
-    if (fold_after != 0 && fold_after != 1) {
-        snprintf(buf, sizeof buf, "fq_pack_weights: fold_after=%d must be 0 or 1", fold_after);
-        return fail(FQ_ERR_ARG, buf);
-    }
-    if (ascale)
-        for (int32_t k = 0; k < K; ++k)
-            if (!(ascale[k] > 0.0f) || !std::isfinite(ascale[k])) {
-                snprintf(buf, sizeof buf, "fq_pack_weights: ascale[%d]=%g must be finite and > 0", k,
-                         double(ascale[k]));
-                return fail(FQ_ERR_ARG, buf);
-            }
-    unsigned nt = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
-    nt = std::min<unsigned>(nt, unsigned(N));
-    std::vector<std::thread> pool;
-    const int32_t per = (N + int32_t(nt) - 1) / int32_t(nt);
-    for (unsigned t = 0; t < nt; ++t) {
-        const int32_t n0 = int32_t(t) * per, n1 = std::min(N, n0 + per);
-        if (n0 >= n1) break;
-        pool.emplace_back(pack_rows, W, n0, n1, K, ascale, fold_after, hblock, wbits,
-                          static_cast<uint8_t*>(codes_out), wscale_out);
-    }
-    for (auto& th : pool) th.join();
+    const fq_status st = check_rows("fq_dequant_rows", N, K, ascale, fold_after, hblock, wbits);
+    if (st != FQ_OK) return st;
+    for (int32_t n = 0; n < N; ++n)
+        if (!(wscale[n] >= 0.0f) || !std::isfinite(wscale[n])) {
+            char buf[128];
+            snprintf(buf, sizeof buf, "fq_dequant_rows: wscale[%d]=%g must be finite and >= 0", n, double(wscale[n]));
+            fq::set_error(buf);
+            return FQ_ERR_ARG;
+        }
+    parallel_rows(N, [&](int32_t n0, int32_t n1) {
+        dequant_rows(static_cast<const uint8_t*>(codes), wscale, n0, n1, K, ascale, fold_after, hblock, wbits, W_out);
+    });
     return FQ_OK;
 }
