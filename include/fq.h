@@ -164,6 +164,26 @@ fq_status fq_linear(const void* x_bf16, int32_t M, int32_t K, int64_t ldx,
                     void* y_bf16, int64_t ldy,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* Head-layout variants (the page's CUDA path fuses "the head layout" into the
+ * epilogue; the SYCL path keeps plain outputs and so has none): the output of
+ * feature n = h * head_dim + d for token m goes to y[h][m][d], i.e. y is
+ * [N / head_dim][M][head_dim], each head a dense [M][head_dim] block (the
+ * layout attention consumes per head).  head_dim must be a positive multiple
+ * of 8 dividing N; everything else, including the row-major [M][ldr]
+ * residual, is as in fq_gemm / fq_linear. */
+fq_status fq_gemm_heads(const void* act_codes, const float* act_scale, int32_t M, int32_t abits,
+                        const void* w_codes, const float* wscale, int32_t N, int32_t K, int32_t wbits,
+                        const float* bias, const void* residual_bf16, int64_t ldr,
+                        int32_t head_dim, void* y_bf16, int32_t* acc_i32, void* stream);
+
+fq_status fq_linear_heads(const void* x_bf16, int32_t M, int32_t K, int64_t ldx,
+                          const float* gamma_folded, float eps, const float* ascale,
+                          int32_t fold_after, int32_t hblock, int32_t abits,
+                          const void* w_codes, const float* wscale, int32_t N, int32_t wbits,
+                          const float* bias, const void* residual_bf16, int64_t ldr,
+                          int32_t head_dim, void* y_bf16,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

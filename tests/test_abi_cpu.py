@@ -233,6 +233,28 @@ def test_gemm_rejects_before_device_work(kw, status, match):
     assert msg.startswith("fq_gemm:") and re.search(match, msg), msg
 
 
+@pytest.mark.parametrize("kw,status,match", [
+    (dict(hd=12), 2, "head_dim=12 is not a multiple of 8"),
+    (dict(hd=48), 2, r"N=128 is not a whole number of heads of head_dim=48 \(128/48 = 2.667\)"),
+    (dict(hd=-8), 2, "head_dim=-8 must be > 0"),
+    (dict(hd=64, y=None), 1, "y_bf16 is NULL"),
+])
+def test_gemm_heads_rejects_before_device_work(kw, status, match):
+    a = dict(hd=64, y=DEV)
+    a.update(kw)
+    rc = fq.lib().fq_gemm_heads(DEV, DEV, 64, 8, DEV, DEV, 128, 256, 8, None, None, 0, a["hd"], a["y"], None, None)
+    assert rc == status
+    msg = fq.last_error()
+    assert msg.startswith("fq_gemm_heads:") and re.search(match, msg), msg
+
+
+def test_linear_heads_rejects_before_device_work():
+    rc = fq.lib().fq_linear_heads(DEV, 16, 256, 256, DEV, 1e-6, None, 0, 64, 8, DEV, DEV, 128, 8, None, None, 0,
+                                  24, DEV, 0x100000, 1 << 20, None)
+    assert rc == 2
+    assert fq.last_error().startswith("fq_linear_heads: head_dim=24") or "head_dim=24" in fq.last_error()
+
+
 def _linear(**kw):
     a = dict(x=DEV, M=16, K=256, ldx=256, gamma=DEV, eps=1e-6, ascale=None, fold_after=0, hblock=64, abits=8,
              w=DEV, sw=DEV, N=128, wbits=8, bias=None, res=None, ldr=0, y=DEV, ldy=128, ws=0x100000,

@@ -120,3 +120,44 @@ def test_gemv_split_k_shapes(shape, bits):
                                                     residual=(M % 2 == 0))
     assert np.array_equal(acc, acc_ref), f"{np.count_nonzero(acc != acc_ref)} accumulators differ"
     assert_y_elementwise(yg, yf, acc_ref, sa, sw, b, res, what=f"gemv M{M} N{N} K{K}")
+
+
+@pytest.mark.parametrize("shape", [(1, 256, 512), (16, 384, 256), (17, 128, 1024), (33, 256, 384), (300, 1152, 768)],
+                         ids=lambda s: "M{}_N{}_K{}".format(*s))
+@pytest.mark.parametrize("bits", [(8, 8), (4, 4)], ids=lambda b: "A{}W{}".format(*b))
+@pytest.mark.parametrize("head_dim", [8, 64, 128])
+def test_gemm_heads_is_the_row_major_output_per_head(shape, bits, head_dim):
+    """fq_gemm_heads writes exactly fq_gemm's outputs, each head's features as a
+    dense [M][head_dim] block: y_heads[h][m][d] == y[m][h * head_dim + d]."""
+    M, N, K = shape
+    if N % head_dim:
+        pytest.skip("N is not a whole number of heads")
+    abits, wbits = bits
+    log(f"gemm heads M={M} N={N} K={K} A{abits}W{wbits} head_dim={head_dim}")
+    rng = np.random.default_rng(M + N + K + head_dim)
+    ca, cw = rand_codes(rng, M, K, abits), rand_codes(rng, N, K, wbits)
+    sa = rng.uniform(0.001, 0.05, M).astype(np.float32)
+    sw = rng.uniform(0.0001, 0.002, N).astype(np.float32)
+    b = (rng.standard_normal(N) * 0.1).astype(np.float32)
+    res = (rng.standard_normal((M, N)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    from w4a4_integer_gemm_amd import fq_gemm, fq_gemm_heads
+    args = (dev(ca), dev(sa), M, abits, dev(cw), dev(sw), N, K, wbits, dev(b), dev(res), N)
+    y = dev(np.zeros((M, N), np.uint16))
+    fq_gemm(*args, y, N, None)
+    yh = dev(np.zeros((N // head_dim, M, head_dim), np.uint16))
+    fq_gemm_heads(*args, head_dim, yh, None)
+    ref = host(y, np.uint16)
+    got = host(yh, np.uint16).transpose(1, 0, 2).reshape(M, N)
+    assert np.array_equal(got, ref)
+
+
+def test_linear_heads_on_the_qkv_shape():
+    """fq_linear_heads on the fused QKV site (head_dim 128: 28 query, 4 key, 4 value heads)."""
+    import synth
+    from w4a4_integer_gemm_amd import DeviceSite
+    wl = synth.make_workload("qkv_w8a8", M=64)
+    site = DeviceSite(wl.W, wl.hblock, wl.wbits, wl.abits, gamma=wl.gamma, ascale=wl.ascale, eps=wl.eps)
+    x = site.upload(wl.x)
+    y = host(site.linear(x), np.uint16)
+    yh = host(site.linear_heads(x, 128), np.uint16)
+    assert np.array_equal(yh.transpose(1, 0, 2).reshape(wl.M, wl.N), y)

@@ -32,9 +32,12 @@ SIGNATURES = {
     "fq_dequant_rows": ([_P, _P, _I32, _I32, _P, _I32, _I32, _I32, _P], ctypes.c_int),
     "fq_prologue": ([_P, _I32, _I32, _I64, _P, _F, _P, _I32, _I32, _I32, _P, _P, _P], ctypes.c_int),
     "fq_gemm": ([_P, _P, _I32, _I32, _P, _P, _I32, _I32, _I32, _P, _P, _I64, _P, _I64, _P, _P], ctypes.c_int),
+    "fq_gemm_heads": ([_P, _P, _I32, _I32, _P, _P, _I32, _I32, _I32, _P, _P, _I64, _I32, _P, _P, _P], ctypes.c_int),
     "fq_linear_workspace_bytes": ([_I32, _I32, _I32], _SZ),
     "fq_linear": ([_P, _I32, _I32, _I64, _P, _F, _P, _I32, _I32, _I32, _P, _P, _I32, _I32, _P, _P, _I64, _P,
                    _I64, _P, _SZ, _P], ctypes.c_int),
+    "fq_linear_heads": ([_P, _I32, _I32, _I64, _P, _F, _P, _I32, _I32, _I32, _P, _P, _I32, _I32, _P, _P, _I64,
+                         _I32, _P, _P, _SZ, _P], ctypes.c_int),
 }
 
 
@@ -163,3 +166,18 @@ def fq_linear(x, M: int, K: int, ldx: int, gamma_folded, eps: float, ascale, fol
     _check(lib().fq_linear(_dptr(x), M, K, ldx, _dptr(gamma_folded), eps, _dptr(ascale), fold_after, hblock, abits,
                            _dptr(w_codes), _dptr(wscale), N, wbits, _dptr(bias), _dptr(residual), ldr, _dptr(y),
                            ldy, _dptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def fq_gemm_heads(act_codes, act_scale, M: int, abits: int, w_codes, wscale, N: int, K: int, wbits: int, bias,
+                  residual, ldr: int, head_dim: int, y, acc=None, stream=None):
+    _check(lib().fq_gemm_heads(_dptr(act_codes), _dptr(act_scale), M, abits, _dptr(w_codes), _dptr(wscale), N, K,
+                               wbits, _dptr(bias), _dptr(residual), ldr, head_dim, _dptr(y), _dptr(acc),
+                               _stream(stream)))
+
+
+def fq_linear_heads(x, M: int, K: int, ldx: int, gamma_folded, eps: float, ascale, fold_after: int, hblock: int,
+                    abits: int, w_codes, wscale, N: int, wbits: int, bias, residual, ldr: int, head_dim: int, y,
+                    workspace, workspace_bytes: int, stream=None):
+    _check(lib().fq_linear_heads(_dptr(x), M, K, ldx, _dptr(gamma_folded), eps, _dptr(ascale), fold_after, hblock,
+                                 abits, _dptr(w_codes), _dptr(wscale), N, wbits, _dptr(bias), _dptr(residual), ldr,
+                                 head_dim, _dptr(y), _dptr(workspace), workspace_bytes, _stream(stream)))

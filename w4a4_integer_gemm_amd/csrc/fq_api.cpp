@@ -108,7 +108,7 @@ fq_status validate_prologue(const char* fn, const void* x, int32_t M, int32_t K,
 fq_status validate_gemm(const char* fn, const void* act, const float* act_scale, int32_t M, int32_t abits,
                         const void* w, const float* wscale, int32_t N, int32_t K, int32_t wbits,
                         const float* bias, const void* residual, int64_t ldr, const void* y, int64_t ldy,
-                        bool check_act) {
+                        bool check_act, int32_t head_dim = 0) {
     if (check_act && !act) return fail(FQ_ERR_ARG, fmt("%s: act_codes is NULL", fn));
     if (check_act && !act_scale) return fail(FQ_ERR_ARG, fmt("%s: act_scale is NULL", fn));
     if (!w) return fail(FQ_ERR_ARG, fmt("%s: w_codes is NULL", fn));
@@ -120,8 +120,18 @@ fq_status validate_gemm(const char* fn, const void* act, const float* act_scale,
     FQ_TRY(check_k(fn, K, kGemmK));
     FQ_TRY(check_bits(fn, "abits", abits));
     FQ_TRY(check_bits(fn, "wbits", wbits));
-    if (ldy < N) return fail(FQ_ERR_SHAPE, fmt("%s: ldy=%lld < N=%d", fn, (long long)ldy, N));
-    if (ldy % 8) return fail(FQ_ERR_ALIGN, fmt("%s: ldy=%lld is not a multiple of 8 bf16", fn, (long long)ldy));
+    if (head_dim > 0) {
+        if (head_dim % 8)
+            return fail(FQ_ERR_SHAPE, fmt("%s: head_dim=%d is not a multiple of 8", fn, head_dim));
+        if (N % head_dim)
+            return fail(FQ_ERR_SHAPE, fmt("%s: N=%d is not a whole number of heads of head_dim=%d (%d/%d = %.3f)", fn,
+                                          N, head_dim, N, head_dim, double(N) / head_dim));
+    } else if (head_dim < 0) {
+        return fail(FQ_ERR_SHAPE, fmt("%s: head_dim=%d must be > 0", fn, head_dim));
+    } else {
+        if (ldy < N) return fail(FQ_ERR_SHAPE, fmt("%s: ldy=%lld < N=%d", fn, (long long)ldy, N));
+        if (ldy % 8) return fail(FQ_ERR_ALIGN, fmt("%s: ldy=%lld is not a multiple of 8 bf16", fn, (long long)ldy));
+    }
     if (residual && ldr < N) return fail(FQ_ERR_SHAPE, fmt("%s: ldr=%lld < N=%d", fn, (long long)ldr, N));
     if (residual && ldr % 8) return fail(FQ_ERR_ALIGN, fmt("%s: ldr=%lld is not a multiple of 8 bf16", fn, (long long)ldr));
     if (check_act && !aligned(act, 16)) return fail(FQ_ERR_ALIGN, fmt("%s: act_codes is not 16-byte aligned", fn));
@@ -194,31 +204,33 @@ fq_status fq_prologue(const void* x_bf16, int32_t M, int32_t K, int64_t ldx, con
     return device_status(fn, fq::launch_prologue(a, static_cast<hipStream_t>(stream)));
 }
 
-fq_status fq_gemm(const void* act_codes, const float* act_scale, int32_t M, int32_t abits, const void* w_codes,
-                  const float* wscale, int32_t N, int32_t K, int32_t wbits, const float* bias,
-                  const void* residual_bf16, int64_t ldr, void* y_bf16, int64_t ldy, int32_t* acc_i32,
-                  void* stream) {
+}  // extern "C"
+
+namespace {
+
+fq_status gemm_impl(const char* fn, const void* act_codes, const float* act_scale, int32_t M, int32_t abits,
+                    const void* w_codes, const float* wscale, int32_t N, int32_t K, int32_t wbits, const float* bias,
+                    const void* residual_bf16, int64_t ldr, void* y_bf16, int64_t ldy, int32_t head_dim,
+                    int32_t* acc_i32, void* stream) {
     fq::clear_error();
-    const char* fn = "fq_gemm";
     FQ_TRY(validate_gemm(fn, act_codes, act_scale, M, abits, w_codes, wscale, N, K, wbits, bias, residual_bf16,
-                         ldr, y_bf16, ldy, true));
-    if (acc_i32 && !aligned(acc_i32, 16)) return fail(FQ_ERR_ALIGN, "fq_gemm: acc_i32 is not 16-byte aligned");
+                         ldr, y_bf16, ldy, true, head_dim));
+    if (acc_i32 && !aligned(acc_i32, 16)) return fail(FQ_ERR_ALIGN, fmt("%s: acc_i32 is not 16-byte aligned", fn));
     fq::GemmArgs g{static_cast<const uint8_t*>(act_codes), act_scale, M, abits,
                    static_cast<const uint8_t*>(w_codes), wscale, N, K, wbits, bias,
                    static_cast<const uint16_t*>(residual_bf16), ldr, static_cast<uint16_t*>(y_bf16), ldy,
-                   acc_i32};
+                   acc_i32, head_dim};
     return run_gemm(fn, g, static_cast<hipStream_t>(stream));
 }
 
-fq_status fq_linear(const void* x_bf16, int32_t M, int32_t K, int64_t ldx, const float* gamma_folded, float eps,
-                    const float* ascale, int32_t fold_after, int32_t hblock, int32_t abits, const void* w_codes,
-                    const float* wscale, int32_t N, int32_t wbits, const float* bias, const void* residual_bf16,
-                    int64_t ldr, void* y_bf16, int64_t ldy, void* workspace, size_t workspace_bytes,
-                    void* stream) {
+fq_status linear_impl(const char* fn, const void* x_bf16, int32_t M, int32_t K, int64_t ldx,
+                      const float* gamma_folded, float eps, const float* ascale, int32_t fold_after, int32_t hblock,
+                      int32_t abits, const void* w_codes, const float* wscale, int32_t N, int32_t wbits,
+                      const float* bias, const void* residual_bf16, int64_t ldr, void* y_bf16, int64_t ldy,
+                      int32_t head_dim, void* workspace, size_t workspace_bytes, void* stream) {
     fq::clear_error();
-    const char* fn = "fq_linear";
-    if (!workspace) return fail(FQ_ERR_ARG, "fq_linear: workspace is NULL");
-    if (!aligned(workspace, 256)) return fail(FQ_ERR_ALIGN, "fq_linear: workspace is not 256-byte aligned");
+    if (!workspace) return fail(FQ_ERR_ARG, fmt("%s: workspace is NULL", fn));
+    if (!aligned(workspace, 256)) return fail(FQ_ERR_ALIGN, fmt("%s: workspace is not 256-byte aligned", fn));
     // shape checks first so that the workspace size below is meaningful
     if (M < 1) return fail(FQ_ERR_SHAPE, fmt("%s: M=%d must be >= 1", fn, M));
     FQ_TRY(check_k(fn, K, kGemmK));
@@ -232,15 +244,55 @@ fq_status fq_linear(const void* x_bf16, int32_t M, int32_t K, int64_t ldx, const
     FQ_TRY(validate_prologue(fn, x_bf16, M, K, ldx, gamma_folded, eps, ascale, fold_after, hblock, abits, codes,
                              scales));
     FQ_TRY(validate_gemm(fn, codes, scales, M, abits, w_codes, wscale, N, K, wbits, bias, residual_bf16, ldr,
-                         y_bf16, ldy, true));
+                         y_bf16, ldy, true, head_dim));
     hipStream_t s = static_cast<hipStream_t>(stream);
     fq::PrologueArgs a{static_cast<const uint16_t*>(x_bf16), M, K, ldx, gamma_folded, eps, ascale,
                        fold_after, hblock, abits, codes, scales};
     FQ_TRY(device_status(fn, fq::launch_prologue(a, s)));
     fq::GemmArgs g{codes, scales, M, abits, static_cast<const uint8_t*>(w_codes), wscale, N, K, wbits, bias,
                    static_cast<const uint16_t*>(residual_bf16), ldr, static_cast<uint16_t*>(y_bf16), ldy,
-                   nullptr};
+                   nullptr, head_dim};
     return run_gemm(fn, g, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+fq_status fq_gemm(const void* act_codes, const float* act_scale, int32_t M, int32_t abits, const void* w_codes,
+                  const float* wscale, int32_t N, int32_t K, int32_t wbits, const float* bias,
+                  const void* residual_bf16, int64_t ldr, void* y_bf16, int64_t ldy, int32_t* acc_i32,
+                  void* stream) {
+    return gemm_impl("fq_gemm", act_codes, act_scale, M, abits, w_codes, wscale, N, K, wbits, bias, residual_bf16,
+                     ldr, y_bf16, ldy, 0, acc_i32, stream);
+}
+
+fq_status fq_gemm_heads(const void* act_codes, const float* act_scale, int32_t M, int32_t abits,
+                        const void* w_codes, const float* wscale, int32_t N, int32_t K, int32_t wbits,
+                        const float* bias, const void* residual_bf16, int64_t ldr, int32_t head_dim, void* y_bf16,
+                        int32_t* acc_i32, void* stream) {
+    return gemm_impl("fq_gemm_heads", act_codes, act_scale, M, abits, w_codes, wscale, N, K, wbits, bias,
+                     residual_bf16, ldr, y_bf16, 0, head_dim, acc_i32, stream);
+}
+
+fq_status fq_linear(const void* x_bf16, int32_t M, int32_t K, int64_t ldx, const float* gamma_folded, float eps,
+                    const float* ascale, int32_t fold_after, int32_t hblock, int32_t abits, const void* w_codes,
+                    const float* wscale, int32_t N, int32_t wbits, const float* bias, const void* residual_bf16,
+                    int64_t ldr, void* y_bf16, int64_t ldy, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+    return linear_impl("fq_linear", x_bf16, M, K, ldx, gamma_folded, eps, ascale, fold_after, hblock, abits,
+                       w_codes, wscale, N, wbits, bias, residual_bf16, ldr, y_bf16, ldy, 0, workspace,
+                       workspace_bytes, stream);
+}
+
+fq_status fq_linear_heads(const void* x_bf16, int32_t M, int32_t K, int64_t ldx, const float* gamma_folded,
+                          float eps, const float* ascale, int32_t fold_after, int32_t hblock, int32_t abits,
+                          const void* w_codes, const float* wscale, int32_t N, int32_t wbits, const float* bias,
+                          const void* residual_bf16, int64_t ldr, int32_t head_dim, void* y_bf16, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+    return linear_impl("fq_linear_heads", x_bf16, M, K, ldx, gamma_folded, eps, ascale, fold_after, hblock, abits,
+                       w_codes, wscale, N, wbits, bias, residual_bf16, ldr, y_bf16, 0, head_dim, workspace,
+                       workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -116,7 +116,8 @@ __device__ __forceinline__ v4i mfma16x16x64(v4i a, v4i b, v4i c) {
 // token m[ii] + lane % 16, with n[i] and m[ii] already including the lane's part:
 //   y[m][n] = bf16_rne(float(acc >> shift) * (s_m * s_n) [+ bias_n] [+ residual_mn])
 // in float32, each step rounded (no contraction); acc_out, when given, receives
-// the exact integer sums.  Every operand is loaded before the first store: on
+// the exact integer sums.  y is [M][ldy], or [N/head_dim][M][head_dim] when
+// head_dim > 0.  Every operand is loaded before the first store: on
 // gfx9 stores count in the same vector-memory counter as loads, so a load placed
 // after a store would wait for that store to complete.
 template <int TN, int TM>
@@ -124,7 +125,8 @@ __device__ __forceinline__ void store_tiles(const v4i (&acc)[TN][TM], int shift,
                                             int M, int N, const float* __restrict__ act_scale,
                                             const float* __restrict__ wscale, const float* __restrict__ bias,
                                             const uint16_t* __restrict__ residual, int64_t ldr,
-                                            uint16_t* __restrict__ y, int64_t ldy, int32_t* __restrict__ acc_out) {
+                                            uint16_t* __restrict__ y, int64_t ldy, int32_t* __restrict__ acc_out,
+                                            int head_dim) {
     float sa[TM];
 #pragma unroll
     for (int ii = 0; ii < TM; ++ii) sa[ii] = m[ii] < M ? act_scale[m[ii]] : 0.0f;
@@ -172,7 +174,12 @@ __device__ __forceinline__ void store_tiles(const v4i (&acc)[TN][TM], int shift,
             uint2 o;
             o.x = f32_to_bf16(t0) | (f32_to_bf16(t1) << 16);
             o.y = f32_to_bf16(t2) | (f32_to_bf16(t3) << 16);
-            *reinterpret_cast<uint2*>(y + int64_t(m[ii]) * ldy + n[i]) = o;
+            uint16_t* yp = y + int64_t(m[ii]) * ldy + n[i];
+            if (head_dim > 0) {  // [N/head_dim][M][head_dim]; 4 consecutive n stay in one head
+                const int h = n[i] / head_dim;
+                yp = y + (int64_t(h) * M + m[ii]) * head_dim + (n[i] - h * head_dim);
+            }
+            *reinterpret_cast<uint2*>(yp) = o;
             if (acc_out) *reinterpret_cast<int4*>(acc_out + int64_t(m[ii]) * N + n[i]) = make_int4(a0, a1, a2, a3);
         }
 }

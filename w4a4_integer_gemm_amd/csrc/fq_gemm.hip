@@ -362,7 +362,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
 
     // ---------------------------------------------------------------- epilogue
     // All eight waves: wave w takes tile rows w BM/8 .. + BM/8; a lane takes 8
-    // consecutive outputs n .. n + 7 of one token (one 16-byte bf16 store):
+    // consecutive outputs n .. n + 7 of one token (one 16-byte bf16 store; in
+    // the head layout the 8 stay inside one head since head_dim % 8 == 0):
     //   y[m][n] = bf16_rne(float(acc >> shift) * (s_m * s_n) [+ bias_n] [+ residual_mn])
     // in float32, one rounding per step.  Every operand is loaded before the
     // first store (a load queued behind a store would wait for it).
@@ -426,7 +427,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
                 }
                 o[e / 2] = f32_to_bf16(t0) | (f32_to_bf16(t1) << 16);
             }
-            *reinterpret_cast<uint4*>(g.y + int64_t(m) * g.ldy + n) = make_uint4(o[0], o[1], o[2], o[3]);
+            *reinterpret_cast<uint4*>(out_ptr(g, m, n)) = make_uint4(o[0], o[1], o[2], o[3]);
             if (g.acc) {
                 int32_t* ap = g.acc + int64_t(m) * g.N + n;
                 *reinterpret_cast<int4*>(ap) = make_int4(a[0], a[1], a[2], a[3]);

@@ -153,7 +153,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(GemmArgs g, int pe
 #pragma unroll
         for (int r = 0; r < R; ++r) nn[r] = n0 + 16 * r + q * 4;
         store_tiles<R, MT>(acc, shift, mm, nn, g.M, g.N, g.act_scale, g.wscale, g.bias, g.residual, g.ldr, g.y, g.ldy,
-                           g.acc);
+                           g.acc, g.head_dim);
         return;
     }
     // tile i = (r, t) = (i / MT, i % MT): wave i sums the S partials of tile i and stores it
@@ -168,7 +168,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(GemmArgs g, int pe
     const int mm[1] = {(wave % MT) * 16 + (lane & 15)};
     const int nn[1] = {n0 + 16 * (wave / MT) + q * 4};
     store_tiles<1, 1>(sum, shift, mm, nn, g.M, g.N, g.act_scale, g.wscale, g.bias, g.residual, g.ldr, g.y, g.ldy,
-                      g.acc);
+                      g.acc, g.head_dim);
 }
 
 // Waves per workgroup: enough that a wave's share fits one batch of C units,

@@ -40,7 +40,17 @@ struct GemmArgs {
     uint16_t* y;
     int64_t ldy;
     int32_t* acc;             // nullptr: not written
+    int32_t head_dim;         // 0: y is [M][ldy]; else y is [N/head_dim][M][head_dim]
 };
+
+// Address of output (m, n) (n a multiple of 4 inside one head when head_dim > 0).
+__host__ __device__ inline uint16_t* out_ptr(const GemmArgs& g, int m, int n) {
+    if (g.head_dim > 0) {
+        const int h = n / g.head_dim;
+        return g.y + (int64_t(h) * g.M + m) * g.head_dim + (n - h * g.head_dim);
+    }
+    return g.y + int64_t(m) * g.ldy + n;
+}
 
 // Enqueue the kernels; they return hipGetLastError() of the launch.
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t stream);

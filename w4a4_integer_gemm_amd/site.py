@@ -99,6 +99,18 @@ class DeviceSite:
                     0 if residual is None else residual.stride(0), y, y.stride(0), ws, ws.numel(), stream)
         return y
 
+    def linear_heads(self, x, head_dim: int, residual=None, y=None, stream=None):
+        """fq_linear_heads: y is [N / head_dim][M][head_dim] (int16 tensor of bf16 bits)."""
+        import torch
+        M = x.shape[0]
+        if y is None:
+            y = torch.empty((self.N // head_dim, M, head_dim), dtype=torch.int16, device=self.device)
+        ws = self.workspace(M)
+        B.fq_linear_heads(x, M, self.K, x.stride(0), self.gamma, self.eps, self.ascale, self.fold_after, self.hblock,
+                          self.abits, self.codes, self.wscale, self.N, self.wbits, self.bias, residual,
+                          0 if residual is None else residual.stride(0), head_dim, y, ws, ws.numel(), stream)
+        return y
+
     def workspace_codes(self, M: int):
         """(codes, scales) views of the workspace after fq_linear."""
         import torch
