@@ -29,7 +29,7 @@ from .build import LIB, build
 __all__ = [
     "lib", "hadamard_entry", "rotate_f64", "butterfly_f32", "fold_gain", "fold_weights",
     "pack_weights", "unfold_weights", "act_frame", "prologue", "gemm_i32", "epilogue",
-    "bf16_from_f64", "code_at", "num_threads", "unpack_codes", "linear", "row_bytes", "qmax",
+    "bf16_from_f64", "code_at", "num_threads", "unpack_codes", "linear", "row_bytes", "qmax", "geglu",
 ]
 
 _lib = None
@@ -57,6 +57,7 @@ def lib():
         L.fqo_act_frame.argtypes = [_P, _I32, _I32, _I64, _P, _F, _P, _I32, _I32, _P]
         L.fqo_prologue.argtypes = [_P, _I32, _I32, _I64, _P, _F, _P, _I32, _I32, _I32, _P, _P]
         L.fqo_gemm_i32.argtypes = [_P, _I32, _I32, _P, _I32, _I32, _I32, _P]
+        L.fqo_geglu.argtypes = [_P, _I32, _I32, _I64, _P, _I64, _P]
         L.fqo_epilogue.argtypes = [_P, _I32, _I32, _P, _P, _P, _P, _I64, _P, _P]
         L.fqo_bf16_from_f64.argtypes = [ctypes.c_double]
         L.fqo_bf16_from_f64.restype = ctypes.c_uint16
@@ -202,6 +203,17 @@ def epilogue(acc, act_scale, wscale, bias=None, residual_bits=None, want_f64: bo
                               _p(_c(wscale, np.float32)), _p(_c(bias, np.float32)), _p(res),
                               N if res is None else res.shape[1], _p(y), _p(yf)), "epilogue")
     return (y, yf) if want_f64 else y
+
+
+def geglu(gu_bits, F: int, want_f64: bool = False):
+    """h = bf16(gelu_tanh(gate) * up) for rows [gate F | up F] (the chained MLP
+    block between the gate+up and down sites); float64 inside, one rounding."""
+    gu = _c(gu_bits, np.uint16)
+    M = gu.shape[0]
+    h = np.empty((M, F), np.uint16)
+    hf = np.empty((M, F), np.float64) if want_f64 else None
+    _check(lib().fqo_geglu(_p(gu), M, F, gu.shape[1], _p(h), F, _p(hf)), "geglu")
+    return (h, hf) if want_f64 else h
 
 
 def bf16_from_f64(v: float) -> int:

@@ -317,6 +317,25 @@ int fqo_epilogue(const int32_t* acc, int32_t M, int32_t N, const float* act_scal
     return 0;
 }
 
+/* GeGLU between the MLP sites of the chained block (gate+up site, GeGLU,
+ * down site with the residual): h = bf16(gelu_tanh(gate) * up), float64 inside,
+ * one rounding; gelu_tanh(g) = g/2 * (1 + tanh(sqrt(2/pi) * (g + 0.044715 g^3))). */
+int fqo_geglu(const uint16_t* gu, int32_t M, int32_t F, int64_t ld_in, uint16_t* h, int64_t ld_out,
+              double* h_f64) {
+    if (!gu || !h || M < 1 || F < 1 || ld_in < 2 * (int64_t)F || ld_out < F) return -1;
+    const double c = sqrt(2.0 / 3.14159265358979323846);
+#pragma omp parallel for schedule(static)
+    for (int32_t m = 0; m < M; ++m)
+        for (int32_t j = 0; j < F; ++j) {
+            const double g = (double)bf16_to_f32(gu[(int64_t)m * ld_in + j]);
+            const double u = (double)bf16_to_f32(gu[(int64_t)m * ld_in + F + j]);
+            const double t = 0.5 * g * (1.0 + tanh(c * (g + 0.044715 * g * g * g))) * u;
+            if (h_f64) h_f64[(int64_t)m * F + j] = t;
+            h[(int64_t)m * ld_out + j] = fqo_bf16_from_f64(t);
+        }
+    return 0;
+}
+
 int fqo_num_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();

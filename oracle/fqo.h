@@ -97,6 +97,12 @@ int fqo_epilogue(const int32_t* acc, int32_t M, int32_t N, const float* act_scal
 /* Nearest-even bfloat16 of a float64 value (one rounding). */
 uint16_t fqo_bf16_from_f64(double v);
 
+/* GeGLU of a gate+up output row [gate F | up F] (bf16) into h (bf16):
+ * h = bf16_rne(gelu_tanh(gate) * up) from float64; h_f64 (optional) receives
+ * the value before rounding. */
+int fqo_geglu(const uint16_t* gu, int32_t M, int32_t F, int64_t ld_in, uint16_t* h, int64_t ld_out,
+              double* h_f64);
+
 /* Threads the oracle's parallel loops use (OpenMP max threads). */
 int fqo_num_threads(void);
 

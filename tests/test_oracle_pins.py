@@ -390,3 +390,36 @@ def test_rotation_reduces_error_on_outlier_site():
         exact = h @ wl.W.astype(np.float64).T
         errs[b] = np.linalg.norm(out["y_f64"] - exact) / np.linalg.norm(exact)
     assert errs[128] < errs[1]
+
+
+def test_geglu_matches_torch_tanh_gelu_and_rounds_once():
+    """GeGLU of the chained MLP block: the float64 value is torch's tanh-approximate
+    GELU (a library routine) times up, and the bf16 output is its single
+    nearest-even rounding."""
+    import torch
+    rng = np.random.default_rng(5)
+    F = 96
+    gu = synth.f32_to_bf16_bits((rng.standard_normal((6, 2 * F)) * 2.5).astype(np.float32))
+    h, hf = oracle.geglu(gu, F, want_f64=True)
+    g = torch.from_numpy(synth.bf16_bits_to_f32(gu[:, :F]).astype(np.float64))
+    u = torch.from_numpy(synth.bf16_bits_to_f32(gu[:, F:]).astype(np.float64))
+    ref = (torch.nn.functional.gelu(g, approximate="tanh") * u).numpy()
+    assert np.allclose(hf, ref, rtol=1e-13, atol=1e-300)
+    want = np.array([[oracle.bf16_from_f64(v) for v in row] for row in ref], np.uint16)
+    assert np.array_equal(h, want)
+
+
+def test_geglu_special_values():
+    """gelu(0) = 0; gelu(g) -> g for large g and -> 0 for very negative g."""
+    one = synth.f32_to_bf16_bits(np.float32(1.0))
+    rows = []
+    for gate in (0.0, 20.0, -20.0, 3.0):
+        rows.append([synth.f32_to_bf16_bits(np.float32(gate)), one])
+    gu = np.array(rows, np.uint16).reshape(4, 2)
+    h, hf = oracle.geglu(gu, 1, want_f64=True)
+    assert hf[0, 0] == 0.0
+    assert abs(hf[1, 0] - 20.0) < 1e-12
+    assert abs(hf[2, 0]) < 1e-12
+    # gelu_tanh(3) from its definition with tanh evaluated by numpy
+    c = np.sqrt(2 / np.pi)
+    assert abs(hf[3, 0] - 1.5 * (1 + np.tanh(c * (3 + 0.044715 * 27)))) < 1e-14
