@@ -164,6 +164,17 @@ fq_status fq_linear(const void* x_bf16, int32_t M, int32_t K, int64_t ldx,
                     void* y_bf16, int64_t ldy,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* GeGLU between the sites of a chained MLP block (gate+up site -> GeGLU -> down
+ * site with the residual, the Gemma-style MLP of the page's pi0.5 backbone):
+ *   h[m][j] = bf16_rne(gelu_tanh(g) * u),  g = gateup[m][j], u = gateup[m][F + j],
+ *   gelu_tanh(g) = g/2 * (1 + tanh(sqrt(2/pi) * (g + 0.044715 g^3)))
+ * in float32 (device tanh).  gateup_bf16: device bf16 [M][ld_in] holding
+ * [gate F | up F] per row (the gate+up site's output); h_bf16: device bf16
+ * [M][ld_out].  F a positive multiple of 8; ld_in >= 2F and ld_out >= F,
+ * multiples of 8; 16-byte aligned bases. */
+fq_status fq_geglu(const void* gateup_bf16, int32_t M, int32_t F, int64_t ld_in,
+                   void* h_bf16, int64_t ld_out, void* stream);
+
 /* Head-layout variants (the page's CUDA path fuses "the head layout" into the
  * epilogue; the SYCL path keeps plain outputs and so has none): the output of
  * feature n = h * head_dim + d for token m goes to y[h][m][d], i.e. y is

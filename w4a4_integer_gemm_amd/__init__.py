@@ -5,14 +5,15 @@ hand-written HIP kernels behind the C ABI declared in include/fq.h.  This
 package only loads that library and marshals arguments; torch provides device
 memory and streams.
 """
-from ._binding import (FqError, abi_version, fq_act_bytes, fq_dequant_rows, fq_fold_gain, fq_gemm, fq_gemm_heads,
+from ._binding import (FqError, abi_version, fq_act_bytes, fq_dequant_rows, fq_fold_gain, fq_geglu, fq_gemm,
+                       fq_gemm_heads,
                        fq_linear, fq_linear_heads,
                        fq_linear_workspace_bytes, fq_pack_weights, fq_prologue, fq_weight_bytes, last_error,
                        lib)
 from .site import DeviceSite
 
 __all__ = [
-    "FqError", "abi_version", "fq_act_bytes", "fq_fold_gain", "fq_gemm", "fq_gemm_heads", "fq_linear",
+    "FqError", "abi_version", "fq_act_bytes", "fq_fold_gain", "fq_geglu", "fq_gemm", "fq_gemm_heads", "fq_linear",
     "fq_linear_heads", "fq_linear_workspace_bytes",
     "fq_pack_weights", "fq_dequant_rows", "fq_prologue", "fq_weight_bytes", "last_error", "lib", "DeviceSite",
 ]

@@ -32,6 +32,7 @@ SIGNATURES = {
     "fq_dequant_rows": ([_P, _P, _I32, _I32, _P, _I32, _I32, _I32, _P], ctypes.c_int),
     "fq_prologue": ([_P, _I32, _I32, _I64, _P, _F, _P, _I32, _I32, _I32, _P, _P, _P], ctypes.c_int),
     "fq_gemm": ([_P, _P, _I32, _I32, _P, _P, _I32, _I32, _I32, _P, _P, _I64, _P, _I64, _P, _P], ctypes.c_int),
+    "fq_geglu": ([_P, _I32, _I32, _I64, _P, _I64, _P], ctypes.c_int),
     "fq_gemm_heads": ([_P, _P, _I32, _I32, _P, _P, _I32, _I32, _I32, _P, _P, _I64, _I32, _P, _P, _P], ctypes.c_int),
     "fq_linear_workspace_bytes": ([_I32, _I32, _I32], _SZ),
     "fq_linear": ([_P, _I32, _I32, _I64, _P, _F, _P, _I32, _I32, _I32, _P, _P, _I32, _I32, _P, _P, _I64, _P,
@@ -181,3 +182,7 @@ def fq_linear_heads(x, M: int, K: int, ldx: int, gamma_folded, eps: float, ascal
     _check(lib().fq_linear_heads(_dptr(x), M, K, ldx, _dptr(gamma_folded), eps, _dptr(ascale), fold_after, hblock,
                                  abits, _dptr(w_codes), _dptr(wscale), N, wbits, _dptr(bias), _dptr(residual), ldr,
                                  head_dim, _dptr(y), _dptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def fq_geglu(gateup, M: int, F: int, ld_in: int, h, ld_out: int, stream=None):
+    _check(lib().fq_geglu(_dptr(gateup), M, F, ld_in, _dptr(h), ld_out, _stream(stream)))

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libfq.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["fq_api.cpp", "fq_pack.cpp", "fq_prologue.hip", "fq_gemm.hip", "fq_gemv.hip"]
+SOURCES = ["fq_api.cpp", "fq_pack.cpp", "fq_prologue.hip", "fq_gemm.hip", "fq_gemv.hip", "fq_geglu.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

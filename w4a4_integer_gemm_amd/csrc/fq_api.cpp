@@ -5,6 +5,8 @@
 // naming the call and argument and showing the arithmetic that failed.
 #include <hip/hip_runtime.h>
 
+#include <climits>
+
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -283,6 +285,28 @@ fq_status fq_linear(const void* x_bf16, int32_t M, int32_t K, int64_t ldx, const
     return linear_impl("fq_linear", x_bf16, M, K, ldx, gamma_folded, eps, ascale, fold_after, hblock, abits,
                        w_codes, wscale, N, wbits, bias, residual_bf16, ldr, y_bf16, ldy, 0, workspace,
                        workspace_bytes, stream);
+}
+
+fq_status fq_geglu(const void* gateup_bf16, int32_t M, int32_t F, int64_t ld_in, void* h_bf16, int64_t ld_out,
+                   void* stream) {
+    fq::clear_error();
+    const char* fn = "fq_geglu";
+    if (!gateup_bf16) return fail(FQ_ERR_ARG, "fq_geglu: gateup_bf16 is NULL");
+    if (!h_bf16) return fail(FQ_ERR_ARG, "fq_geglu: h_bf16 is NULL");
+    if (M < 1) return fail(FQ_ERR_SHAPE, fmt("%s: M=%d must be >= 1", fn, M));
+    if (F < 8 || F % 8) return fail(FQ_ERR_SHAPE, fmt("%s: F=%d must be a positive multiple of 8", fn, F));
+    if (int64_t(M) * (F / 8) > int64_t(INT32_MAX) * 256)
+        return fail(FQ_ERR_SHAPE, fmt("%s: M=%d x F=%d is too large for one launch", fn, M, F));
+    if (ld_in < 2 * int64_t(F))
+        return fail(FQ_ERR_SHAPE, fmt("%s: ld_in=%lld < 2F=%lld", fn, (long long)ld_in, 2 * (long long)F));
+    if (ld_in % 8) return fail(FQ_ERR_ALIGN, fmt("%s: ld_in=%lld is not a multiple of 8 bf16", fn, (long long)ld_in));
+    if (ld_out < F) return fail(FQ_ERR_SHAPE, fmt("%s: ld_out=%lld < F=%d", fn, (long long)ld_out, F));
+    if (ld_out % 8) return fail(FQ_ERR_ALIGN, fmt("%s: ld_out=%lld is not a multiple of 8 bf16", fn, (long long)ld_out));
+    if (!aligned(gateup_bf16, 16)) return fail(FQ_ERR_ALIGN, "fq_geglu: gateup_bf16 is not 16-byte aligned");
+    if (!aligned(h_bf16, 16)) return fail(FQ_ERR_ALIGN, "fq_geglu: h_bf16 is not 16-byte aligned");
+    return device_status(fn, fq::launch_geglu(static_cast<const uint16_t*>(gateup_bf16), M, F, ld_in,
+                                              static_cast<uint16_t*>(h_bf16), ld_out,
+                                              static_cast<hipStream_t>(stream)));
 }
 
 fq_status fq_linear_heads(const void* x_bf16, int32_t M, int32_t K, int64_t ldx, const float* gamma_folded,

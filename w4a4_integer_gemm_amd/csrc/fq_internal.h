@@ -56,6 +56,8 @@ __host__ __device__ inline uint16_t* out_ptr(const GemmArgs& g, int m, int n) {
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t stream);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_gemv(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_geglu(const uint16_t* gu, int32_t M, int32_t F, int64_t ld_in, uint16_t* h, int64_t ld_out,
+                        hipStream_t stream);
 
 // Largest M that the GEMV kernel takes.
 constexpr int32_t kGemvMaxM = 32;
