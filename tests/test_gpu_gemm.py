@@ -102,20 +102,29 @@ def test_gemm_every_tile_shape(tile, bits, monkeypatch):
 
 
 GEMV_SHAPES = [
-    # M, N, K: the GEMV splits K over 1..8 waves of a workgroup and walks each
-    # wave's share in batches; these cover one and several batches, shares that
-    # do not divide K evenly, a last wave with nothing to do, and M on both
-    # sides of 16
+    # M, N, K: both GEMV kernels split K over the waves of a workgroup and walk
+    # each wave's share in batches; these cover one and several batches, shares
+    # that do not divide K evenly, a last wave with nothing to do, and M on both
+    # sides of 16.  The streaming kernel (codes in LDS) takes 5 <= M <= 32 when
+    # the codes fit; M <= 4, K = 18944 and 65536 (and K = 16384 at 8-bit codes)
+    # stay on the split-K kernel either way.  N = 8200 .. 16400 gives a
+    # streaming workgroup several row groups.
     (1, 24, 1408), (2, 40, 1152), (15, 8, 640), (16, 72, 2304), (17, 24, 896),
     (31, 16, 4608), (32, 8, 18944), (1, 3592, 3584), (16, 8, 65536), (3, 2056, 8192),
+    (1, 16400, 256), (16, 8200, 2304), (32, 10248, 640), (5, 1032, 16384), (8, 16400, 3584),
 ]
 
 
 @pytest.mark.parametrize("shape", GEMV_SHAPES, ids=lambda s: "M{}_N{}_K{}".format(*s))
 @pytest.mark.parametrize("bits", [(8, 8), (4, 4), (8, 4), (4, 8)], ids=lambda b: "A{}W{}".format(*b))
-def test_gemv_split_k_shapes(shape, bits):
+@pytest.mark.parametrize("kernel", ["default", "split"])
+def test_gemv_split_k_shapes(shape, bits, kernel, monkeypatch):
+    """Decode-sized M through the default kernel choice and through the split-K
+    kernel forced by the FQ_GEMV=split test hook."""
     M, N, K = shape
-    log(f"gemv M={M} N={N} K={K} A{bits[0]}W{bits[1]}")
+    if kernel == "split":
+        monkeypatch.setenv("FQ_GEMV", "split")
+    log(f"gemv {kernel} M={M} N={N} K={K} A{bits[0]}W{bits[1]}")
     acc, acc_ref, yg, yf, sa, sw, b, res = run_gemm(M, N, K, bits[0], bits[1], seed=M + N + K, bias=True,
                                                     residual=(M % 2 == 0))
     assert np.array_equal(acc, acc_ref), f"{np.count_nonzero(acc != acc_ref)} accumulators differ"

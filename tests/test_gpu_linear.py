@@ -106,3 +106,16 @@ def test_dequant_float_path_agrees_with_integer_path(name, max_rel):
     cos = float(np.sum(y_int * y_float) / (np.linalg.norm(y_int) * np.linalg.norm(y_float)))
     log(f"dequant vs integer {name}: rel {rel:.3e} cosine {cos:.6f}")
     assert rel <= max_rel and cos >= 1 - max_rel ** 2
+
+
+
+def test_decode_with_changing_token_counts():
+    """One site (one workspace) serving decode calls with different M, as a
+    serving loop would: both GEMV kernels (split-K below 5 tokens, streaming
+    above) against the oracle on every token."""
+    wl = synth.random_workload(32, 1024, 1032, 64, 8, 8, seed=5, norm=True, ascale="gain")
+    site = site_for(wl)
+    site.workspace(32)
+    for M in (32, 1, 16, 3, 32, 1, 17, 5):
+        sub = synth.Workload(**{**wl.__dict__, "x": wl.x[:M], "M": M})
+        check_linear(sub, site, what=f"M={M}")

@@ -16,6 +16,10 @@
 // per tile runs the epilogue.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <cstdlib>
+#include <cstring>
+
 #include "fq_device.h"
 #include "fq_internal.h"
 
@@ -203,10 +207,243 @@ void launch_bits(const GemmArgs& g, hipStream_t st) {
         launch_cfg<ABITS, WBITS, 2, 2, 8>(g, st);
 }
 
+
+// ---------------------------------------------------------------------------
+// Persistent streaming GEMV: the decode path for 5 <= M <= 32 whenever the
+// tokens' codes fit in LDS.
+//
+// The split-K kernel above reads each activation unit from L2 once per row
+// group; from M = 8 on those reads cost more than they save (at M = 16 they
+// are half as large as the weight stream itself).  Here each workgroup copies
+// the M tokens' codes into LDS once and then walks a contiguous range of
+// 16-row groups.  Seven waves split K: a wave streams its share of a group in
+// chunks of CH 16-byte loads (8, or 4 with two token tiles, which need twice
+// the activation registers) and keeps the next chunk (of the same or the
+// next group) in flight while it consumes one, and it touches no other global
+// memory, so nothing else waits behind its loads.  At the end of a group the
+// seven partial tiles meet in LDS (double-buffered: one barrier per group)
+// and the eighth wave runs the epilogue (scales, bias, residual, stores)
+// while the others stream on.  A launch has as many workgroups as are
+// resident at once, so the codes are copied a few hundred times in all.
+constexpr int kStreamWaves = 8;  // waves per workgroup
+constexpr int kLoadWaves = 7;    // waves that stream the weights; the last one stores
+constexpr int kMaxLds = 160 * 1024;
+constexpr int kStreamMinM = 5;   // below, the split-K kernel streams faster (its act reads are tiny)
+
+// LDS row pitch of the codes: >= kb and 16 more than a multiple of 256, so the
+// 16 token rows of a fragment start 4 banks apart.
+__host__ __device__ inline int act_pitch(int kb) { return (kb + 239) / 256 * 256 + 16; }
+
+// codes [16 MT][pitch] | partial tiles [2][7][MT][64] v4i | the tokens' scales [32]
+__host__ __device__ inline size_t stream_lds_bytes(int mt, int pitch) {
+    return size_t(16 * mt) * size_t(pitch) + size_t(2 * kLoadWaves * mt) * 64 * 16 + 128;
+}
+
+template <int ABITS, int WBITS>
+__device__ __forceinline__ void lds_act(ActReg& a, const uint8_t* p) {
+    using U = Unit<ABITS, WBITS>;
+    a.v[1] = make_uint4(0, 0, 0, 0);
+    if (U::ALANE == 8) {
+        const uint2 t = *reinterpret_cast<const uint2*>(p);
+        a.v[0] = make_uint4(t.x, t.y, 0, 0);
+    } else {
+        a.v[0] = *reinterpret_cast<const uint4*>(p);
+        if (U::AREGS == 2) a.v[1] = *reinterpret_cast<const uint4*>(p + 16);
+    }
+}
+
+// grid: resident workgroups, each with a contiguous range of the `groups`
+// 16-row groups; block: 8 waves (at most 128 VGPRs: two workgroups per CU
+// when LDS allows).
+template <int ABITS, int WBITS, int MT>
+__global__ __launch_bounds__(64 * kStreamWaves) __attribute__((amdgpu_waves_per_eu(4))) void stream_kernel(
+    GemmArgs g, int pitch, int groups) {
+    using U = Unit<ABITS, WBITS>;
+    constexpr int CH = MT == 1 ? 8 : 4;
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    uint8_t* const act_lds = smem;
+    v4i* const red = reinterpret_cast<v4i*>(smem + 16 * MT * pitch);
+    float* const scale_lds = reinterpret_cast<float*>(smem + 16 * MT * pitch + 2 * kLoadWaves * MT * 64 * 16);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int q = lane >> 4;
+    const bool loader = wave < kLoadWaves;
+    const int nu = g.K / U::K;
+    const int per = (nu + kLoadWaves - 1) / kLoadWaves;
+    const int u_begin = loader && wave * per < nu ? wave * per : nu;
+    const int u_end = u_begin + per < nu ? u_begin + per : nu;  // >= 1
+    const int nb = (per + CH - 1) / CH;                 // chunks per group
+    const int gb = int(int64_t(blockIdx.x) * groups / gridDim.x);
+    const int ge = int(int64_t(blockIdx.x + 1) * groups / gridDim.x);
+    const int J = (ge - gb) * nb;
+    const int64_t ldw = int64_t(g.K) * WBITS / 8;
+
+    // chunk j = (group gb + j / nb, units u_begin + CH (j % nb) + [0, CH));
+    // units past the wave's share reload its last unit and are not used, so
+    // every chunk is exactly CH loads
+    auto issue = [&](uint4 (&w)[CH], int j) {
+        const int jg = j / nb;
+        const int b = j - jg * nb;
+        int row = (gb + jg) * 16 + (lane & 15);
+        row = row < g.N ? row : g.N - 1;  // rows past N load a valid row; their outputs are not stored
+        const uint8_t* p = g.w + int64_t(row) * ldw + q * 16;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            int u = u_begin + b * CH + c;
+            u = u < u_end ? u : u_end - 1;
+            w[c] = *reinterpret_cast<const uint4*>(p + int64_t(u) * U::WROW);
+        }
+    };
+
+    // chunk j lives in buffer j % 2; a step issues chunk j + 1 (the last chunk
+    // again at the end: unused) and then consumes chunk j
+    uint4 wa[CH], wb[CH];
+    const int last = J - 1;
+    if (loader && J > 0) issue(wa, 0);
+
+    // the tokens' codes and scales into LDS; rows M .. 16 MT - 1 are zero
+    {
+        const int kb = g.K * ABITS / 8;
+        const int pieces = kb >> 4;
+        const int total = 16 * MT * pieces;
+        for (int i = tid; i < total; i += 64 * kStreamWaves) {
+            const int r = i / pieces;
+            const int cc = i - r * pieces;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (r < g.M) v = *reinterpret_cast<const uint4*>(g.act + int64_t(r) * kb + cc * 16);
+            *reinterpret_cast<uint4*>(act_lds + r * pitch + cc * 16) = v;
+        }
+        if (tid < g.M) scale_lds[tid] = g.act_scale[tid];
+    }
+    __syncthreads();
+
+    constexpr int shift = AccShift<ABITS, WBITS>::value;
+    if (!loader) {
+        // the storing wave: one barrier per group, then the group's epilogue
+        for (int gi = gb, buf = 0; gi < ge; ++gi, buf ^= 1) {
+            __syncthreads();
+            const v4i* const rb = red + buf * (kLoadWaves * MT * 64);
+            v4i sum[1][MT];
+            int mm[MT];
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                sum[0][t] = rb[t * 64 + lane];
+#pragma unroll
+                for (int w = 1; w < kLoadWaves; ++w) sum[0][t] += rb[(w * MT + t) * 64 + lane];
+                mm[t] = t * 16 + (lane & 15);
+            }
+            const int nn[1] = {gi * 16 + q * 4};
+            store_tiles<1, MT>(sum, shift, mm, nn, g.M, g.N, scale_lds, g.wscale, g.bias, g.residual, g.ldr, g.y,
+                               g.ldy, g.acc, g.head_dim);
+        }
+        return;
+    }
+    v4i acc[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[t] = v4i{0, 0, 0, 0};
+    int buf = 0;
+    const uint8_t* const arow = act_lds + (lane & 15) * pitch + q * U::ALANE;
+    auto step = [&](uint4 (&cur)[CH], uint4 (&nxt)[CH], int j) {
+        issue(nxt, j + 1 < last ? j + 1 : last);
+        const int b = j % nb;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int u = u_begin + b * CH + c;
+            if (u < u_end) {  // wave-uniform
+#pragma unroll
+                for (int t = 0; t < MT; ++t) {
+                    ActReg a;
+                    lds_act<ABITS, WBITS>(a, arow + t * 16 * pitch + u * U::AROW);
+                    acc[t] = unit_mfma<ABITS, WBITS>(cur[c], a, acc[t]);
+                }
+            }
+        }
+        if (b == nb - 1) {  // the group is done: partial tiles -> LDS for the storing wave
+            v4i* const rb = red + buf * (kLoadWaves * MT * 64);
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                rb[(wave * MT + t) * 64 + lane] = acc[t];
+                acc[t] = v4i{0, 0, 0, 0};
+            }
+            __syncthreads();
+            buf ^= 1;
+        }
+    };
+    for (int j = 0; j < J; j += 2) {
+        step(wa, wb, j);
+        if (j + 1 < J) step(wb, wa, j + 1);
+    }
+}
+
+int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+int stream_mt(int M) { return M <= 16 ? 1 : 2; }
+
+bool stream_fits(const GemmArgs& g) {
+    if (g.M < kStreamMinM || g.M > kGemvMaxM) return false;
+    const char* e = std::getenv("FQ_GEMV");  // test hook: "split" keeps the split-K kernel
+    if (e && std::strcmp(e, "split") == 0) return false;
+    return stream_lds_bytes(stream_mt(g.M), act_pitch(g.K * g.abits / 8)) <= size_t(kMaxLds);
+}
+
+template <int ABITS, int WBITS, int MT>
+hipError_t launch_stream_t(const GemmArgs& g, hipStream_t st) {
+    const int pitch = act_pitch(g.K * ABITS / 8);
+    const size_t lds = stream_lds_bytes(MT, pitch);
+    const auto kern = stream_kernel<ABITS, WBITS, MT>;
+    // resident workgroups per CU for the last LDS size (the codes' share changes with K)
+    static std::atomic<int64_t> occ{-1};
+    int64_t o = occ.load(std::memory_order_relaxed);
+    int per_cu;
+    if (o >= 0 && (o >> 8) == int64_t(lds)) {
+        per_cu = int(o & 0xFF);
+    } else {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
+        if (e != hipSuccess) return e;
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * kStreamWaves, lds);
+        if (e != hipSuccess) return e;
+        if (per_cu < 1) return hipErrorInvalidValue;
+        per_cu = per_cu > 255 ? 255 : per_cu;
+        occ.store((int64_t(lds) << 8) | per_cu, std::memory_order_relaxed);
+    }
+    const int cus = device_cus();
+    if (cus < 1) return hipErrorInvalidDevice;
+    const int groups = (g.N + 15) / 16;
+    const int grid = groups < per_cu * cus ? groups : per_cu * cus;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * kStreamWaves), lds, st, g, pitch, groups);
+    return hipGetLastError();
+}
+
+template <int ABITS, int WBITS>
+hipError_t launch_stream_bits(const GemmArgs& g, hipStream_t st) {
+    return stream_mt(g.M) == 1 ? launch_stream_t<ABITS, WBITS, 1>(g, st) : launch_stream_t<ABITS, WBITS, 2>(g, st);
+}
+
+hipError_t launch_stream(const GemmArgs& g, hipStream_t st) {
+    if (g.abits == 8 && g.wbits == 8) return launch_stream_bits<8, 8>(g, st);
+    if (g.abits == 4 && g.wbits == 4) return launch_stream_bits<4, 4>(g, st);
+    if (g.abits == 8 && g.wbits == 4) return launch_stream_bits<8, 4>(g, st);
+    return launch_stream_bits<4, 8>(g, st);
+}
+
 }  // namespace
 
 hipError_t launch_gemv(const GemmArgs& g, hipStream_t stream) {
     if (g.M > kGemvMaxM) return hipErrorInvalidValue;
+    if (stream_fits(g)) return launch_stream(g, stream);
     if (g.abits == 8 && g.wbits == 8)
         launch_bits<8, 8>(g, stream);
     else if (g.abits == 4 && g.wbits == 4)
