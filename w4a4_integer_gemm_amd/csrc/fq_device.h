@@ -23,11 +23,11 @@ __device__ __forceinline__ uint2 load_stream8(const uint8_t* p) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// float32 -> bfloat16 bits, round to nearest, ties to even (NaN -> quiet NaN).
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-    const uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+// Two float32 -> bfloat16 conversions packed in one dword (lo in the low half),
+// round to nearest, ties to even: gfx950's v_cvt_pk_bf16_f32 (NaN -> quiet NaN).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    const __bf16 a = static_cast<__bf16>(lo), b = static_cast<__bf16>(hi);
+    return uint32_t(__builtin_bit_cast(uint16_t, a)) | (uint32_t(__builtin_bit_cast(uint16_t, b)) << 16);
 }
 
 // Operand fragments for v_mfma_i32_16x16x64_i8.  The MFMA sums over its 64 k
@@ -172,8 +172,8 @@ __device__ __forceinline__ void store_tiles(const v4i (&acc)[TN][TM], int shift,
                 t3 = t3 + bf16_hi(rs[i][ii].y);
             }
             uint2 o;
-            o.x = f32_to_bf16(t0) | (f32_to_bf16(t1) << 16);
-            o.y = f32_to_bf16(t2) | (f32_to_bf16(t3) << 16);
+            o.x = pack_bf16x2(t0, t1);
+            o.y = pack_bf16x2(t2, t3);
             uint16_t* yp = y + int64_t(m[ii]) * ldy + n[i];
             if (head_dim > 0) {  // [N/head_dim][M][head_dim]; 4 consecutive n stay in one head
                 const int h = n[i] / head_dim;

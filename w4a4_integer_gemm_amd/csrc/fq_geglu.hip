@@ -36,7 +36,7 @@ __global__ __launch_bounds__(256) void geglu_kernel(const uint16_t* __restrict__
     for (int i = 0; i < 4; ++i) {
         const float lo = gelu_tanh(bf16_lo(gw[i])) * bf16_lo(uw[i]);
         const float hi = gelu_tanh(bf16_hi(gw[i])) * bf16_hi(uw[i]);
-        o[i] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+        o[i] = pack_bf16x2(lo, hi);
     }
     *reinterpret_cast<uint4*>(h + int64_t(m) * ld_out + j) = make_uint4(o[0], o[1], o[2], o[3]);
 }

@@ -188,6 +188,45 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
     const bool half_last = (g.K % CF::KS) != 0;
     const int nfull = nk - (half_last ? 1 : 0);
 
+    // Epilogue operands.  All eight waves store: wave w takes tile rows
+    // w BM/8 .. + BM/8; a lane takes 8 consecutive outputs n .. n + 7 of one
+    // token (one 16-byte bf16 store; in the head layout the 8 stay inside one
+    // head since head_dim % 8 == 0).  Each wave issues these loads as soon as
+    // its part of the main loop is done, so that their latency hides behind
+    // the exchange of the two k halves.
+    constexpr int LPR = CF::BNS / 8;   // lanes per token row
+    constexpr int RPI = 64 / LPR;      // token rows per pass
+    constexpr int ROWS = CF::BM / 8;   // token rows per wave
+    constexpr int NIT = (ROWS + RPI - 1) / RPI;
+    const int lr = lane / LPR, lc = lane % LPR;
+    const int n_epi = n0 + 8 * lc;
+    const bool col_ok = lr < RPI && n_epi < g.N;
+    float4 sw0 = make_float4(0.f, 0.f, 0.f, 0.f), sw1 = sw0, b0 = sw0, b1 = sw0;
+    bool ok[NIT];
+    int rr[NIT];
+    float sa[NIT];
+    uint4 rs[NIT];
+    auto load_epilogue_operands = [&]() {
+        if (col_ok) {
+            sw0 = *reinterpret_cast<const float4*>(g.wscale + n_epi);
+            sw1 = *reinterpret_cast<const float4*>(g.wscale + n_epi + 4);
+            if (g.bias) {
+                b0 = *reinterpret_cast<const float4*>(g.bias + n_epi);
+                b1 = *reinterpret_cast<const float4*>(g.bias + n_epi + 4);
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            rr[it] = wave * ROWS + it * RPI + lr;
+            const int m = m0 + rr[it];
+            ok[it] = col_ok && it * RPI + lr < ROWS && m < g.M;
+            sa[it] = ok[it] ? g.act_scale[m] : 0.0f;
+            rs[it] = (ok[it] && g.residual)
+                         ? *reinterpret_cast<const uint4*>(g.residual + int64_t(m) * g.ldr + n_epi)
+                         : make_uint4(0, 0, 0, 0);
+        }
+    };
+
     if (wave >= 4) {
         // ---------------------------------------------------------- load waves
         // Load wave p issues the stage's 1 KB copies c = p + 4 i; a wave with one
@@ -251,6 +290,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
             barrier_nofence();
         }
         wait_vmcnt<0>();      // every ring load has landed
+        load_epilogue_operands();
         barrier_nofence();    // E1: the ring is idle
         barrier_nofence();    // E2: k-half 1 partial sums staged
         barrier_nofence();    // E3: tile complete
@@ -321,6 +361,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
         for (int s = 0; s < nfull; ++s) stage(s, std::true_type{});
         if (half_last) stage(nk - 1, std::false_type{});
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's ring reads are done
+        load_epilogue_operands();
         barrier_nofence();                   // E1: the ring is idle
 
         // Stage the accumulator tile X[BM][BNC] (int32, row stride XS) in the
@@ -361,45 +402,14 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
     }
 
     // ---------------------------------------------------------------- epilogue
-    // All eight waves: wave w takes tile rows w BM/8 .. + BM/8; a lane takes 8
-    // consecutive outputs n .. n + 7 of one token (one 16-byte bf16 store; in
-    // the head layout the 8 stay inside one head since head_dim % 8 == 0):
     //   y[m][n] = bf16_rne(float(acc >> shift) * (s_m * s_n) [+ bias_n] [+ residual_mn])
-    // in float32, one rounding per step.  Every operand is loaded before the
+    // in float32, one rounding per step.  Every operand was loaded before the
     // first store (a load queued behind a store would wait for it).
     {
         const int32_t* X = reinterpret_cast<const int32_t*>(lds);
         constexpr int XS = acc_stride<CF>();
-        constexpr int LPR = CF::BNS / 8;   // lanes per token row
-        constexpr int RPI = 64 / LPR;      // token rows per pass
-        constexpr int ROWS = CF::BM / 8;   // token rows per wave
-        constexpr int NIT = (ROWS + RPI - 1) / RPI;
         constexpr int shift = AccShift<ABITS, WBITS>::value;
-        const int lr = lane / LPR, lc = lane % LPR;
-        const int n = n0 + 8 * lc;
-        const bool col_ok = lr < RPI && n < g.N;
-        float4 sw0 = make_float4(0.f, 0.f, 0.f, 0.f), sw1 = sw0, b0 = sw0, b1 = sw0;
-        if (col_ok) {
-            sw0 = *reinterpret_cast<const float4*>(g.wscale + n);
-            sw1 = *reinterpret_cast<const float4*>(g.wscale + n + 4);
-            if (g.bias) {
-                b0 = *reinterpret_cast<const float4*>(g.bias + n);
-                b1 = *reinterpret_cast<const float4*>(g.bias + n + 4);
-            }
-        }
-        bool ok[NIT];
-        int rr[NIT];
-        float sa[NIT];
-        uint4 rs[NIT];
-#pragma unroll
-        for (int it = 0; it < NIT; ++it) {
-            rr[it] = wave * ROWS + it * RPI + lr;
-            const int m = m0 + rr[it];
-            ok[it] = col_ok && it * RPI + lr < ROWS && m < g.M;
-            sa[it] = ok[it] ? g.act_scale[m] : 0.0f;
-            rs[it] = (ok[it] && g.residual) ? *reinterpret_cast<const uint4*>(g.residual + int64_t(m) * g.ldr + n)
-                                            : make_uint4(0, 0, 0, 0);
-        }
+        const int n = n_epi;
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
@@ -425,7 +435,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
                     t0 = t0 + bf16_lo(rw[e / 2]);
                     t1 = t1 + bf16_hi(rw[e / 2]);
                 }
-                o[e / 2] = f32_to_bf16(t0) | (f32_to_bf16(t1) << 16);
+                o[e / 2] = pack_bf16x2(t0, t1);
             }
             *reinterpret_cast<uint4*>(out_ptr(g, m, n)) = make_uint4(o[0], o[1], o[2], o[3]);
             if (g.acc) {
