@@ -215,8 +215,10 @@ void launch_bits(const GemmArgs& g, hipStream_t st) {
 // The split-K kernel above reads each activation unit from L2 once per row
 // group; from M = 8 on those reads cost more than they save (at M = 16 they
 // are half as large as the weight stream itself).  Here each workgroup copies
-// the M tokens' codes into LDS once and then walks a contiguous range of
-// 16-row groups.  Seven waves split K: a wave streams its share of a group in
+// the M tokens' codes into LDS once and then walks the 16-row groups
+// blockIdx, blockIdx + gridDim, ... (so that at any time the workgroups
+// stream one contiguous band of the weights; contiguous ranges per workgroup
+// measured 5 % slower).  Seven waves split K: a wave streams its share of a group in
 // chunks of CH 16-byte loads (8, or 4 with two token tiles, which need twice
 // the activation registers) and keeps the next chunk (of the same or the
 // next group) in flight while it consumes one, and it touches no other global
@@ -252,7 +254,7 @@ __device__ __forceinline__ void lds_act(ActReg& a, const uint8_t* p) {
     }
 }
 
-// grid: resident workgroups, each with a contiguous range of the `groups`
+// grid: resident workgroups, each taking every gridDim-th of the `groups`
 // 16-row groups; block: 8 waves (at most 128 VGPRs: two workgroups per CU
 // when LDS allows).
 template <int ABITS, int WBITS, int MT>
@@ -275,18 +277,19 @@ __global__ __launch_bounds__(64 * kStreamWaves) __attribute__((amdgpu_waves_per_
     const int u_begin = loader && wave * per < nu ? wave * per : nu;
     const int u_end = u_begin + per < nu ? u_begin + per : nu;  // >= 1
     const int nb = (per + CH - 1) / CH;                 // chunks per group
-    const int gb = int(int64_t(blockIdx.x) * groups / gridDim.x);
-    const int ge = int(int64_t(blockIdx.x + 1) * groups / gridDim.x);
-    const int J = (ge - gb) * nb;
+    // group i of this workgroup is blockIdx + i gridDim (gridDim <= groups)
+    const int gcount = (groups - int(blockIdx.x) + int(gridDim.x) - 1) / int(gridDim.x);
+    const int J = gcount * nb;
+    auto group_of = [&](int i) { return int(blockIdx.x) + i * int(gridDim.x); };
     const int64_t ldw = int64_t(g.K) * WBITS / 8;
 
-    // chunk j = (group gb + j / nb, units u_begin + CH (j % nb) + [0, CH));
+    // chunk j = (group j / nb of this workgroup, units u_begin + CH (j % nb) + [0, CH));
     // units past the wave's share reload its last unit and are not used, so
     // every chunk is exactly CH loads
     auto issue = [&](uint4 (&w)[CH], int j) {
         const int jg = j / nb;
         const int b = j - jg * nb;
-        int row = (gb + jg) * 16 + (lane & 15);
+        int row = group_of(jg) * 16 + (lane & 15);
         row = row < g.N ? row : g.N - 1;  // rows past N load a valid row; their outputs are not stored
         const uint8_t* p = g.w + int64_t(row) * ldw + q * 16;
 #pragma unroll
@@ -322,7 +325,8 @@ __global__ __launch_bounds__(64 * kStreamWaves) __attribute__((amdgpu_waves_per_
     constexpr int shift = AccShift<ABITS, WBITS>::value;
     if (!loader) {
         // the storing wave: one barrier per group, then the group's epilogue
-        for (int gi = gb, buf = 0; gi < ge; ++gi, buf ^= 1) {
+        for (int i = 0, buf = 0; i < gcount; ++i, buf ^= 1) {
+            const int gi = group_of(i);
             __syncthreads();
             const v4i* const rb = red + buf * (kLoadWaves * MT * 64);
             v4i sum[1][MT];
