@@ -14,7 +14,9 @@ from fqtest import assert_codes, dev, host, log
 pytestmark = pytest.mark.gpu
 
 CASES = [
-    # M, K, hblock, abits, norm, ascale mode, fold_after
+    # M, K, hblock, abits, norm, ascale mode, fold_after.  Values per lane: 16 for
+    # K <= 8192 (a 256-block then spans 16 lanes: the xor-8 exchange), 32 up to
+    # K = 32768, 64 beyond
     (1, 64, 1, 8, False, "none", 0),
     (3, 64, 64, 4, True, "gain", 0),
     (16, 256, 64, 8, True, "gain", 0),
@@ -28,8 +30,10 @@ CASES = [
     (64, 3584, 128, 8, True, "gain", 0),
     (8, 3584, 128, 4, False, "explicit", 1),
     (4, 8192, 128, 8, True, "none", 0),
-    (3, 8256, 64, 8, True, "gain", 0),      # 64 values per lane, 129 lanes
-    (3, 8224, 32, 4, True, "none", 0),      # K % 64 = 32 -> 32 values per lane, 257 lanes
+    (3, 8160, 32, 8, True, "gain", 0),      # 16 values per lane, 510 lanes (last wave ragged)
+    (5, 7936, 256, 4, True, "gain", 0),     # 16 per lane, 256-blocks over 16 lanes
+    (3, 8256, 64, 8, True, "gain", 0),      # 32 values per lane, 258 lanes
+    (3, 8224, 32, 4, True, "none", 0),      # 32 values per lane, 257 lanes
     (2, 32768, 256, 8, False, "explicit", 1),
     (6, 16384, 128, 4, False, "none", 0),
     (5, 18944, 128, 8, False, "none", 0),

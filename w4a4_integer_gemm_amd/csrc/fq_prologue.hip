@@ -3,13 +3,14 @@
 // RMSNorm with the folded gain, the ascale divide, the block rotation, a
 // per-token amax scale, round-half-even and a clamp).
 //
-// Layout: one workgroup per token.  Lane t owns E = 16 (K <= 8192, b <= 128),
-// 32 (K <= 32768) or 64 consecutive bf16 values (E/8 16-byte loads), so a
-// token of up to 65536 values is one pass of at most 1024 lanes.  The butterfly's first log2(E) stages
-// (span 1 .. E/2) run inside a lane's registers; a Hadamard block of b > E
-// values spans b/E consecutive lanes, whose stages (span E .. b/2) exchange
-// values with DPP lane permutations (xor 1, xor 2, and xor 4 composed from two
-// permutations) and one fused multiply-add per value.  Every element goes
+// Layout: one workgroup per token.  Lane t owns E = 16 (K <= 8192), 32
+// (K <= 32768) or 64 consecutive bf16 values (E/8 16-byte loads), so a token
+// of up to 65536 values is one pass of at most 1024 lanes.  The butterfly's
+// first log2(E) stages (span 1 .. E/2) run inside a lane's registers; a
+// Hadamard block of b > E values spans b/E (at most 16) consecutive lanes,
+// whose stages (span E .. b/2) exchange values with DPP lane permutations
+// (xor 1, xor 2, and xor 4 and xor 8 composed from two permutations) and one
+// fused multiply-add per value.  Every element goes
 // through the same float32 operations in the same order as the definition
 // (stage spans 1, 2, 4, ...), so the rotation is bit-reproducible.  The token
 // stays in registers between the two reductions (sum of squares, amax): x is
@@ -87,15 +88,20 @@ __device__ __forceinline__ double wave_sum(double v) {
     return v;
 }
 
-// value held by lane (lane ^ d) of the same wave, d in {1, 2, 4}, via DPP
+// value held by lane (lane ^ d) of the same wave, d in {1, 2, 4, 8}, via DPP
 template <int D>
 __device__ __forceinline__ float lane_xor(float v) {
     const int i = __float_as_int(v);
     if (D == 1) return __int_as_float(__builtin_amdgcn_mov_dpp(i, 0xB1, 0xF, 0xF, true));  // quad_perm [1,0,3,2]
     if (D == 2) return __int_as_float(__builtin_amdgcn_mov_dpp(i, 0x4E, 0xF, 0xF, true));  // quad_perm [2,3,0,1]
-    // xor 4 = (xor 7 within 8 lanes: row_half_mirror) then (xor 3: quad_perm [3,2,1,0])
-    const int m = __builtin_amdgcn_mov_dpp(i, 0x141, 0xF, 0xF, true);
-    return __int_as_float(__builtin_amdgcn_mov_dpp(m, 0x1B, 0xF, 0xF, true));
+    if (D == 4) {
+        // xor 4 = (xor 7 within 8 lanes: row_half_mirror) then (xor 3: quad_perm [3,2,1,0])
+        const int m = __builtin_amdgcn_mov_dpp(i, 0x141, 0xF, 0xF, true);
+        return __int_as_float(__builtin_amdgcn_mov_dpp(m, 0x1B, 0xF, 0xF, true));
+    }
+    // xor 8 = (xor 15 within 16 lanes: row_mirror) then (xor 7: row_half_mirror)
+    const int m = __builtin_amdgcn_mov_dpp(i, 0x140, 0xF, 0xF, true);
+    return __int_as_float(__builtin_amdgcn_mov_dpp(m, 0x141, 0xF, 0xF, true));
 }
 
 // one cross-lane butterfly stage: the lower lane of each pair keeps lo + hi,
@@ -254,6 +260,7 @@ __global__ __launch_bounds__(kMaxThreads) void prologue_kernel(const uint16_t* _
     if constexpr (hblock > E) cross_stage<1, E>(v, lane);
     if constexpr (hblock > 2 * E) cross_stage<2, E>(v, lane);
     if constexpr (hblock > 4 * E) cross_stage<4, E>(v, lane);
+    if constexpr (hblock > 8 * E) cross_stage<8, E>(v, lane);
 #pragma unroll
     for (int i = 0; i < E; ++i) v[i] = v[i] * rs;
 
@@ -275,12 +282,13 @@ __global__ __launch_bounds__(kMaxThreads) void prologue_kernel(const uint16_t* _
     // qmax + 1/2 and round-half-even never leaves [-qmax, qmax]: the clamp of
     // the definition is implied and not executed.
     if (active) {
+        constexpr int G = E < 16 ? E : 16;  // codes per store
 #pragma unroll
-        for (int grp = 0; grp < E / 16; ++grp) {
-            uint32_t t[16];
+        for (int grp = 0; grp < E / G; ++grp) {
+            uint32_t t[G];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float h = v[16 * grp + i];
+            for (int i = 0; i < G; ++i) {
+                const float h = v[G * grp + i];
                 float qf;
                 if (fast) {
                     const float q0 = h * r;
@@ -292,25 +300,33 @@ __global__ __launch_bounds__(kMaxThreads) void prologue_kernel(const uint16_t* _
                 t[i] = round_to_code_bits(qf);
             }
             if (ABITS == 8) {
-                uint32_t w[4];
+                uint32_t w[G / 4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
+                for (int i = 0; i < G / 4; ++i) {
                     // byte 0 of t[4i .. 4i+3] -> one dword
                     const uint32_t lo = __builtin_amdgcn_perm(t[4 * i + 1], t[4 * i + 0], 0x0C0C0400u);
                     const uint32_t hi = __builtin_amdgcn_perm(t[4 * i + 3], t[4 * i + 2], 0x0C0C0400u);
                     w[i] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
                 }
-                *reinterpret_cast<uint4*>(codes + int64_t(m) * K + E * c + 16 * grp) = make_uint4(w[0], w[1], w[2], w[3]);
+                uint8_t* dst = codes + int64_t(m) * K + E * c + G * grp;
+                if constexpr (G == 16)
+                    *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+                else
+                    *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
             } else {
-                uint32_t w[2];
+                uint32_t w[G / 8];
 #pragma unroll
-                for (int i = 0; i < 2; ++i) {
+                for (int i = 0; i < G / 8; ++i) {
                     uint32_t acc = 0;
 #pragma unroll
                     for (int j = 0; j < 8; ++j) acc |= (t[8 * i + j] & 0xFu) << (4 * j);
                     w[i] = acc;
                 }
-                *reinterpret_cast<uint2*>(codes + int64_t(m) * (K / 2) + (E / 2) * c + 8 * grp) = make_uint2(w[0], w[1]);
+                uint8_t* dst = codes + int64_t(m) * (K / 2) + (E / 2) * c + (G / 2) * grp;
+                if constexpr (G == 16)
+                    *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+                else
+                    *reinterpret_cast<uint32_t*>(dst) = w[0];
             }
         }
     }
@@ -357,13 +373,13 @@ hipError_t launch_modes(dim3 grid, dim3 block, hipStream_t st, const PrologueArg
 
 }  // namespace
 
-// Values per lane: 16 up to K = 8192 when a Hadamard block spans at most 8
-// lanes (b <= 128): each token is a chain of dependent steps, and halving a
-// lane's share shortens it (measured on the qkv prologue, K = 3584: 7.0 -> 6.0
-// us for 1024 tokens, 4.0 -> 3.4 us for one); 32 up to K = 32768 (one pass of
-// at most 1024 lanes), 64 beyond.
+// Values per lane: 16 up to K = 8192: each token is a chain of dependent
+// steps, and halving a lane's share shortens it (measured on the qkv prologue,
+// K = 3584: 7.0 -> 6.0 us for 1024 tokens, 4.0 -> 3.4 us for one; 8 per lane
+// gained nothing more); 32 up to K = 32768 (one pass of at most 1024 lanes),
+// 64 beyond.
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t stream) {
-    const int E = (a.K <= 8192 && a.hblock <= 128) ? 16 : a.K > 32768 ? 64 : 32;
+    const int E = a.K <= 8192 ? 16 : a.K > 32768 ? 64 : 32;
     const int nlanes = a.K / E;
     const int T = (nlanes + 63) / 64 * 64;
     if (T > kMaxThreads) return hipErrorInvalidValue;
