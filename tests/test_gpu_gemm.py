@@ -87,6 +87,14 @@ def test_gemm_strided_output_and_residual():
         assert_y_elementwise(yg, yf, acc_ref, sa, sw, None, res, what=f"strided M={M}")
 
 
+def _tile_case(tile, bits):
+    for M, N, K in ((300, 392, 768), (33, 1000, 1280)):
+        acc, acc_ref, yg, yf, sa, sw, b, res = run_gemm(M, N, K, bits[0], bits[1], seed=M + N, bias=True,
+                                                        residual=True)
+        assert np.array_equal(acc, acc_ref), f"{tile}: {np.count_nonzero(acc != acc_ref)} accumulators differ"
+        assert_y_elementwise(yg, yf, acc_ref, sa, sw, b, res, what=f"{tile} M{M} N{N} K{K}")
+
+
 @pytest.mark.parametrize("tile", TILES)
 @pytest.mark.parametrize("bits", [(8, 8), (4, 4), (8, 4), (4, 8)], ids=lambda b: "A{}W{}".format(*b))
 def test_gemm_every_tile_shape(tile, bits, monkeypatch):
@@ -94,11 +102,17 @@ def test_gemm_every_tile_shape(tile, bits, monkeypatch):
     on a ragged problem: M and N not multiples of the tile, several k stages."""
     monkeypatch.setenv("FQ_GEMM_TILE", tile)
     log(f"gemm tile {tile} bits {bits}")
-    for M, N, K in ((300, 392, 768), (33, 1000, 1280)):
-        acc, acc_ref, yg, yf, sa, sw, b, res = run_gemm(M, N, K, bits[0], bits[1], seed=M + N, bias=True,
-                                                        residual=True)
-        assert np.array_equal(acc, acc_ref), f"{tile}: {np.count_nonzero(acc != acc_ref)} accumulators differ"
-        assert_y_elementwise(yg, yf, acc_ref, sa, sw, b, res, what=f"{tile} M{M} N{N} K{K}")
+    _tile_case(tile, bits)
+
+
+@pytest.mark.parametrize("tile", TILES)
+def test_gemm_every_tile_shape_32x32x32_form(tile, monkeypatch):
+    """8-bit x 8-bit codes take v_mfma_i32_16x16x64_i8 by default; the 32x32x32
+    form (FQ_GEMM_MFMA=32 test hook) must give the same exact sums."""
+    monkeypatch.setenv("FQ_GEMM_TILE", tile)
+    monkeypatch.setenv("FQ_GEMM_MFMA", "32")
+    log(f"gemm tile {tile} 32x32x32 form")
+    _tile_case(tile, (8, 8))
 
 
 GEMV_SHAPES = [

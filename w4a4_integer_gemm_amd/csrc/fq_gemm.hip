@@ -5,10 +5,15 @@
 // weight codes with per-shape tiling and the residual add in the epilogue).
 // Integer sums are exact in any order, so tile shape and k order are free.
 //
-// Structure (one 256-thread workgroup = 4 waves per BM x BNS output tile):
+// Structure (one 512-thread workgroup = 4 MFMA waves + 4 load waves per
+// BM x BNS output tile):
 //   - MFMA: v_mfma_i32_32x32x32_i8 with the weight fragment (32 rows n) as the
 //     A operand and the token fragment (32 tokens m) as B; lane l holds token
 //     l % 32 of the result and rows n = 8 g + 4 (l / 32) + i in register 4 g + i.
+//     8-bit x 8-bit codes use v_mfma_i32_16x16x64_i8 instead (the MF16 form:
+//     16-row fragments, so no padded rows for a 144-row tile, and a higher
+//     sustained rate under the power limit); lane l then holds token l % 16
+//     and rows n = 4 (l / 16) + i.
 //   - k advances in stages of 128 (256 with a 4-bit operand).  A stage of the
 //     two operand tiles is copied global -> LDS with global_load_lds_dwordx4 (no
 //     VGPR staging); NS stages live in an LDS ring, so NS-1 stages of loads are
@@ -76,7 +81,7 @@ __device__ __forceinline__ void barrier_nofence() {
     asm volatile("" ::: "memory");
 }
 
-template <int ABITS, int WBITS, int BM_, int BNS_, int BNC_, int NS_, int KS8 = 128>
+template <int ABITS, int WBITS, int BM_, int BNS_, int BNC_, int NS_, int KS8 = 128, bool MF16_ = false>
 struct Cfg {
     // BM tokens x BNS stored weight rows per tile; BNC >= BNS rows are computed
     // (a multiple of 32: the MFMA's row count); rows past BNS belong to the next
@@ -94,13 +99,29 @@ struct Cfg {
     static constexpr int TN = BNC / 32;   // 32-row weight fragments per wave
     static constexpr int TN0 = (TN + 1) / 2;  // output fragments stored by the k-half 0 wave
     static constexpr int NLO = C / 4, NHI = (C + 3) / 4;
+    // MF16: v_mfma_i32_16x16x64_i8 instead of 32x32x32 (8-bit codes only): rows
+    // in fragments of 16, one 64-deep k step per wave per stage, TF16 token
+    // and TW16 row fragments per wave, weight fragments read D16 - 1 ahead
+    // through a ring of D16 registers (D16 divides TW16, so every stage starts
+    // at ring slot 0; at least 3, or 5 when a fragment feeds only two MFMAs)
+    static constexpr bool MF16 = MF16_;
+    static constexpr int TF16 = BM / 32;
+    static constexpr int TW16 = BNC / 16;
+    static constexpr int ring16() {
+        const int need = TF16 >= 4 ? 3 : 5;
+        for (int d = need; d < TW16; ++d)
+            if (TW16 % d == 0) return d;
+        return TW16;
+    }
+    static constexpr int D16 = ring16();
     static_assert(BM == 64 || BM == 128, "two waves of 32 or 64 tokens");
-    static_assert(BNC % 32 == 0 && BNC >= BNS, "computed rows in whole MFMA fragments");
+    static_assert(BNC % (MF16 ? 16 : 32) == 0 && BNC >= BNS, "computed rows in whole MFMA fragments");
+    static_assert(!MF16 || (ABITS == 8 && WBITS == 8 && KS == 128), "the 16x16x64 path takes 8-bit codes");
     static_assert((BM * RA) % 1024 == 0 && (BNC * RW) % 1024 == 0, "whole 1 KB loads");
     static_assert(LDS <= 163840, "LDS ring exceeds 160 KiB");
     static_assert(NS >= 3, "the ring needs a slot being filled, one ready and one being read");
     static_assert((NS - 2) * NHI < 64, "vmcnt range");
-    static_assert(LDS >= 2 * TMF * TN * 4096, "the split-k exchange reuses the ring");
+    static_assert(MF16 || LDS >= 2 * TMF * TN * 4096, "the split-k exchange reuses the ring");
 };
 
 typedef int v16i __attribute__((ext_vector_type(16)));
@@ -134,6 +155,13 @@ __device__ __forceinline__ int operand_offset(int lane, int j) {
     const int rho = lane & 31, h = lane >> 5;
     if (BITS == 8) return 16 * slot_of<R>(rho, 2 * j + h);  // 16 k = 16 bytes
     return 16 * slot_of<R>(rho, j) + 8 * h;                 // 16 k = 8 bytes
+}
+
+// The same for v_mfma_i32_16x16x64_i8 with 8-bit codes: lane l serves row
+// l % 16 of the fragment and k = 64 s + 16 (l / 16) + [0, 16) of 64-deep step s.
+template <int R>
+__device__ __forceinline__ int operand_offset16(int lane, int s) {
+    return 16 * slot_of<R>(lane & 15, 4 * s + (lane >> 4));
 }
 
 template <int BITS, int PARTNER>
@@ -294,6 +322,91 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
         barrier_nofence();    // E1: the ring is idle
         barrier_nofence();    // E2: k-half 1 partial sums staged
         barrier_nofence();    // E3: tile complete
+    } else if constexpr (CF::MF16) {
+        // ------------------------------------------- MFMA waves, 16x16x64 form
+        // wave roles: tokens wm * BM/2 .. + BM/2 (TF16 fragments of 16), all BNC
+        // weight rows (TW16 fragments of 16), 64-deep k step kh of every stage.
+        // Weight fragment p of a stage is read while the MFMAs of fragment
+        // p - (D - 1) run; the reads that would start the next stage wait for
+        // this wave's reads of the stage and for the barrier that publishes it.
+        constexpr int TF = CF::TF16, TW = CF::TW16, D = CF::D16;
+        const int wm = wave & 1;
+        const int kh = wave >> 1;
+        const int offa = operand_offset16<CF::RA>(lane, kh) + wm * (CF::BM / 2) * CF::RA;
+        const int offw = operand_offset16<CF::RW>(lane, kh) + CF::CA * 1024;
+        v4i acc[TW][TF];
+#pragma unroll
+        for (int n = 0; n < TW; ++n)
+#pragma unroll
+            for (int f = 0; f < TF; ++f) acc[n][f] = v4i{0, 0, 0, 0};
+        v4i fa[2][TF], ring[D];
+        auto read_a = [&](int s, int b) {
+            const uint8_t* base = lds + (s % CF::NS) * CF::STAGE + offa;
+#pragma unroll
+            for (int f = 0; f < TF; ++f)
+                fa[b][f] = frag_from_bytes(*reinterpret_cast<const uint4*>(base + f * 16 * CF::RA));
+        };
+        auto read_w = [&](int s, int n) {
+            return frag_from_bytes(
+                *reinterpret_cast<const uint4*>(lds + (s % CF::NS) * CF::STAGE + offw + n * 16 * CF::RW));
+        };
+        barrier_nofence();  // stage 0 published
+        read_a(0, 0);
+#pragma unroll
+        for (int q = 0; q < D - 1; ++q) ring[q] = read_w(0, q);
+        auto stage16 = [&](int s, auto buf_tag) {
+            constexpr int B = decltype(buf_tag)::value;
+            const bool has_next = s + 1 < nk;
+#pragma unroll
+            for (int n = 0; n < TW; ++n) {
+                const int q = n + D - 1;  // the fragment read in this iteration
+                if (q < TW) {
+                    ring[q % D] = read_w(s, q);
+                } else {
+                    if (q == TW) {
+                        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave is done with stage s
+                        barrier_nofence();
+                        if (has_next) read_a(s + 1, B ^ 1);
+                    }
+                    if (has_next) ring[q % D] = read_w(s + 1, q - TW);
+                }
+#pragma unroll
+                for (int f = 0; f < TF; ++f) acc[n][f] = mfma16x16x64(ring[n % D], fa[B][f], acc[n][f]);
+            }
+        };
+        for (int s = 0; s < nk; s += 2) {
+            stage16(s, std::integral_constant<int, 0>{});
+            if (s + 1 < nk) stage16(s + 1, std::integral_constant<int, 1>{});
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's ring reads are done
+        load_epilogue_operands();
+        barrier_nofence();                   // E1: the ring is idle
+
+        // k-half 1 partial sums into X, then k-half 0 adds its own.  Lane l
+        // holds token wm BM/2 + 16 f + l % 16 and rows 16 n + 4 (l / 16) + [0, 4).
+        int32_t* X = reinterpret_cast<int32_t*>(lds);
+        constexpr int XS = acc_stride<CF>();
+        auto xrow = [&](int f, int n) {
+            const int m = wm * (CF::BM / 2) + 16 * f + (lane & 15);
+            return reinterpret_cast<v4i*>(X + m * XS + 16 * n + 4 * (lane >> 4));
+        };
+        if (kh == 1) {
+#pragma unroll
+            for (int n = 0; n < TW; ++n)
+#pragma unroll
+                for (int f = 0; f < TF; ++f) *xrow(f, n) = acc[n][f];
+        }
+        barrier_nofence();  // E2
+        if (kh == 0) {
+#pragma unroll
+            for (int n = 0; n < TW; ++n)
+#pragma unroll
+                for (int f = 0; f < TF; ++f) {
+                    v4i* p = xrow(f, n);
+                    *p = acc[n][f] + *p;
+                }
+        }
+        barrier_nofence();  // E3
     } else {
         // ---------------------------------------------------------- MFMA waves
         // wave roles: tokens wm * BM/2 .. + BM/2 (TMF fragments of 32), all BNC
@@ -473,10 +586,15 @@ constexpr int ring_depth() {
     return n > 8 ? 8 : n;
 }
 
-// Test hook: FQ_GEMM_KS=64 runs 8-bit x 8-bit GEMMs with 64-deep stages.
-int stage_override() {
-    const char* e = std::getenv("FQ_GEMM_KS");
-    return e ? std::atoi(e) : 0;
+// MFMA form of 8-bit x 8-bit GEMMs: v_mfma_i32_16x16x64_i8 (rows in fragments
+// of 16, so a 144-row tile computes no padding rows) unless the test hook
+// FQ_GEMM_MFMA=32 asks for v_mfma_i32_32x32x32_i8.  The 16x16x64 form measured
+// 6-7 % faster on the qkv and down layers (22.8 against 24.6 us, 73.9 against
+// 79.1 us), also where no rows are padded: with random operands it sustains a
+// higher rate under the power limit (3.4-3.6 against 3.2-3.3 POP/s).
+int mfma_form() {
+    const char* e = std::getenv("FQ_GEMM_MFMA");
+    return e ? std::atoi(e) : 16;
 }
 
 template <int ABITS, int WBITS, int BM, int BNS>
@@ -484,8 +602,11 @@ hipError_t launch_shape(const GemmArgs& g, hipStream_t st) {
     constexpr int bnc = (BNS + 31) / 32 * 32;
     constexpr int ns = ring_depth<ABITS, WBITS, BM, bnc>();
     if constexpr (ABITS == 8 && WBITS == 8) {
-        constexpr int ns64 = ring_depth<ABITS, WBITS, BM, bnc, 64>();
-        if (stage_override() == 64) return launch_cfg<ABITS, WBITS, Cfg<ABITS, WBITS, BM, BNS, bnc, ns64, 64>>(g, st);
+        if (mfma_form() == 16) {
+            constexpr int bnc16 = (BNS + 15) / 16 * 16;
+            constexpr int ns16 = ring_depth<ABITS, WBITS, BM, bnc16>();
+            return launch_cfg<ABITS, WBITS, Cfg<ABITS, WBITS, BM, BNS, bnc16, ns16, 128, true>>(g, st);
+        }
     }
     if constexpr (ns >= 3) {
         return launch_cfg<ABITS, WBITS, Cfg<ABITS, WBITS, BM, BNS, bnc, ns>>(g, st);
@@ -520,18 +641,21 @@ hipError_t launch_tile(int tile, const GemmArgs& g, hipStream_t st) {
 }
 
 // Pick the tile that minimises (waves of 256 workgroups) x (computed tile area
-// / relative efficiency): 64-token tiles reuse each weight fragment half as
-// often.  Measured over all eight shapes, the 64-token tiles run at 0.86-0.93
-// of the 128-token rate per unit of area; with 0.9 the model picks the fastest
-// measured tile on each 1024- and 816-token prefill layer: 128 x 144 for QKV
-// (N = 4608, 256 tiles), 64 x 224 for the down projection (N = 3584, 256
-// tiles, where 128 x 128 leaves 32 CUs idle), 128 x 128 for a W4A4 gate+up
-// (N = 32768) and 64 x 128 for its down projection (N = 2048).
-int choose_tile(int M, int N) {
+// / relative efficiency); computed rows are the stored ones rounded up to the
+// MFMA's fragment (16 rows for the 8-bit 16x16x64 form, 32 otherwise).
+// 64-token tiles reuse each weight fragment half as often: measured over all
+// eight shapes they run at 0.86-0.93 of the 128-token rate per unit of area.
+// With 0.9 the model picks the fastest measured tile on each 1024- and
+// 816-token prefill layer: 128 x 144 for QKV (N = 4608, 256 tiles; 22.3 us
+// against 23.5 for 64 x 288), 128 x 112 for the W8A8 down projection (N =
+// 3584, 256 tiles; 69.2 us against 70.7 for 64 x 224 and 78.0 for 128 x 128,
+// which leaves 32 CUs idle), 128 x 128 for a W4A4 gate+up (N = 32768) and
+// 64 x 128 for its down projection (N = 2048).
+int choose_tile(int M, int N, int frag_rows) {
     int best = T128x128;
     double best_cost = 1e300;
     for (int c = 0; c < kNumTiles; ++c) {
-        const int bm = kTileBM[c], bn = kTileBN[c], bnc = (bn + 31) / 32 * 32;
+        const int bm = kTileBM[c], bn = kTileBN[c], bnc = (bn + frag_rows - 1) / frag_rows * frag_rows;
         const long tiles = long((M + bm - 1) / bm) * long((N + bn - 1) / bn);
         const long waves = (tiles + 255) / 256;
         const double eff = bm == 128 ? 1.0 : 0.9;
@@ -557,7 +681,7 @@ int tile_override() {
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream) {
     int tile = tile_override();
-    if (tile < 0) tile = choose_tile(g.M, g.N);
+    if (tile < 0) tile = choose_tile(g.M, g.N, g.abits == 8 && g.wbits == 8 && mfma_form() == 16 ? 16 : 32);
     if (g.abits == 8 && g.wbits == 8) return launch_tile<8, 8>(tile, g, stream);
     if (g.abits == 4 && g.wbits == 4) return launch_tile<4, 4>(tile, g, stream);
     if (g.abits == 8 && g.wbits == 4) return launch_tile<8, 4>(tile, g, stream);
