@@ -51,6 +51,33 @@ def time_loop(fn, iters):
     return e0.elapsed_time(e1) / iters
 
 
+def timed_steps(step, steps, batch=20):
+    """Time `steps` back-to-back calls between two synchronizations (the value
+    reported); HIP events recorded every `batch` calls inside the same region
+    give the spread: median, p10 and p90 of the batch means (ms per call)."""
+    import torch
+    s = torch.cuda.current_stream()
+    marks = []
+    t0 = time.perf_counter()
+    for i in range(steps):
+        if i % batch == 0:
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(s)
+            marks.append((i, e))
+        step()
+    end = torch.cuda.Event(enable_timing=True)
+    end.record(s)
+    marks.append((steps, end))
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    means = [a[1].elapsed_time(b[1]) / (b[0] - a[0]) for a, b in zip(marks, marks[1:]) if b[0] - a[0] == batch]
+    stats = None
+    if means:
+        stats = {"batch": batch, "batches": len(means), "median_ms": float(np.median(means)),
+                 "p10_ms": float(np.percentile(means, 10)), "p90_ms": float(np.percentile(means, 90))}
+    return ms, stats
+
+
 def bench_prefill(name, steps, warmup):
     import torch
     import synth
@@ -64,12 +91,7 @@ def bench_prefill(name, steps, warmup):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms = (t1 - t0) * 1e3 / steps
+    ms, batches = timed_steps(step, steps)
     ops = 2.0 * wl.M * wl.N * wl.K
     codes, scales = site.workspace_codes(wl.M)
     # per-kernel averages (HIP events around back-to-back launches of one kernel)
@@ -79,7 +101,7 @@ def bench_prefill(name, steps, warmup):
     torch.cuda.synchronize()
     ok, detail = parity(wl, site, y, codes, scales)
     return dict(wl=wl, ms=ms, tops=ops / (ms * 1e-3) / 1e12, ms_prologue=ms_pro, ms_gemm=ms_gemm,
-                gemm_tops=ops / (ms_gemm * 1e-3) / 1e12, parity=detail, parity_ok=ok, ops=ops)
+                gemm_tops=ops / (ms_gemm * 1e-3) / 1e12, parity=detail, parity_ok=ok, ops=ops, batches=batches)
 
 
 def parity(wl, site, y, codes, scales, nrows=8):
@@ -127,11 +149,7 @@ def bench_decode(name, steps, warmup, copies=5):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        step()
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / steps
+    ms, batches = timed_steps(step, steps)
     wbytes = wl.N * wl.K * wl.wbits / 8
     # algorithmic bytes: weight codes + weight scales + x + y + activation codes written and read back
     nbytes = wbytes + 4 * wl.N + 2 * wl.M * wl.K + 2 * wl.M * wl.N + 2 * wl.M * wl.K * wl.abits / 8 + 8 * wl.M
@@ -148,7 +166,7 @@ def bench_decode(name, steps, warmup, copies=5):
     ms_gemv = time_loop(gemv, steps)
     gemv_bytes = wbytes + 4 * wl.N + wl.M * wl.K * wl.abits / 8 + 4 * wl.M + 2 * wl.M * wl.N
     return dict(name=name, M=wl.M, ms=ms, gbs=nbytes / (ms * 1e-3) / 1e9, ms_gemv=ms_gemv,
-                gemv_gbs=gemv_bytes / (ms_gemv * 1e-3) / 1e9, bytes=nbytes, gemv_bytes=gemv_bytes)
+                gemv_gbs=gemv_bytes / (ms_gemv * 1e-3) / 1e9, bytes=nbytes, gemv_bytes=gemv_bytes, batches=batches)
 
 
 def cpu_baseline(name, min_seconds=10.0, max_reps=400):
@@ -168,9 +186,43 @@ def cpu_baseline(name, min_seconds=10.0, max_reps=400):
             break
     t = float(np.median(times))
     ops = 2.0 * wl.M * wl.N * wl.K
-    return dict(value=ops / t / 1e12, unit="TOPS", cores=oracle.num_threads(), kind="oracle",
-                sample=f"whole {name} fq_linear (M={wl.M} K={wl.K} N={wl.N}) on the oracle, "
-                       f"{len(times)} repetitions ({sum(times):.1f} s), median {t * 1e3:.1f} ms; weights packed once")
+    out = dict(value=ops / t / 1e12, unit="TOPS", cores=oracle.num_threads(), kind="oracle",
+               sample=f"whole {name} fq_linear (M={wl.M} K={wl.K} N={wl.N}) on the oracle, "
+                      f"{len(times)} repetitions ({sum(times):.1f} s), median {t * 1e3:.1f} ms; weights packed once")
+    out["one_core"] = cpu_one_core(name)
+    return out
+
+
+ONE_CORE_SCRIPT = """
+import json, sys, time
+sys.path.insert(0, {root!r})
+import numpy as np, oracle, synth
+wl = synth.make_workload({name!r}, M={m})
+codes_w, wscale = oracle.pack_weights(wl.W, wl.ascale, wl.fold_after, wl.hblock, wl.wbits)
+ts = []
+t_start = time.perf_counter()
+while time.perf_counter() - t_start < {seconds} or len(ts) < 2:
+    t0 = time.perf_counter()
+    oracle.linear(wl, codes_w=codes_w, wscale=wscale)
+    ts.append(time.perf_counter() - t0)
+t = float(np.median(ts))
+print(json.dumps(dict(value=2.0 * wl.M * wl.N * wl.K / t / 1e12, unit="TOPS", cores=oracle.num_threads(),
+                      sample=f"{{wl.M}} tokens of {name} (K={{wl.K}} N={{wl.N}}), {{len(ts)}} repetitions, "
+                             f"median {{t * 1e3:.1f}} ms")))
+"""
+
+
+def cpu_one_core(name, tokens=64, seconds=4.0):
+    """The same oracle on one host core (OMP_NUM_THREADS=1, a child process that
+    never touches the GPU) over the first `tokens` tokens: the per-core rate."""
+    import subprocess
+    code = ONE_CORE_SCRIPT.format(root=ROOT, name=name, m=tokens, seconds=seconds)
+    env = {**os.environ, "OMP_NUM_THREADS": "1"}
+    try:
+        p = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120)
+        return json.loads(p.stdout.strip().splitlines()[-1]) if p.returncode == 0 else None
+    except (subprocess.SubprocessError, ValueError, IndexError):
+        return None
 
 
 def gemm_bytes(wl):
@@ -243,17 +295,26 @@ def main():
                 "algorithmic_bytes": gemm_bytes(wl)}
     secondary = []
     if not args.no_secondary:
-        for name in ("down_w8a8",):
+        # the other 1024-token prefill shape (part of the headline metric), then the
+        # W4A4 Gemma-shaped MLP sites (parity configs, reported for completeness)
+        for name in ("down_w8a8", "gateup_w4a4", "down_w4a4"):
             s = bench_prefill(name, max(20, args.steps // 4), args.warmup)
             secondary.append({"workload": name, "metric": "fq_linear TOPS", "value": s["tops"],
                               "frac_int8_peak": s["tops"] / PEAK_INT8_TOPS, "ms_per_call": s["ms"],
-                              "gemm_tops": s["gemm_tops"], "ms_prologue": s["ms_prologue"],
-                              "ms_gemm": s["ms_gemm"], "parity": s["parity"]})
+                              "batch_spread": s["batches"], "gemm_tops": s["gemm_tops"],
+                              "ms_prologue": s["ms_prologue"], "ms_gemm": s["ms_gemm"], "parity": s["parity"]})
             del s
+            torch.cuda.empty_cache()
+        # the tiny 16-token site: latency only
+        s = bench_prefill("tiny_w8a8", max(50, args.steps), args.warmup)
+        secondary.append({"workload": "tiny_w8a8", "metric": "fq_linear latency", "value": s["ms"] * 1e3,
+                          "unit": "us", "batch_spread": s["batches"], "parity": s["parity"]})
+        del s
         for name in ("decode_m1_w8a8", "decode_m16_w8a8"):
             d = bench_decode(name, max(50, args.steps), args.warmup)
             secondary.append({"workload": name, "metric": "decode GB/s", "value": d["gbs"],
                               "frac_hbm": d["gbs"] / PEAK_HBM_GBS, "ms_per_call": d["ms"],
+                              "batch_spread": d["batches"],
                               "gemv_gbs": d["gemv_gbs"], "gemv_frac_hbm": d["gemv_gbs"] / PEAK_HBM_GBS,
                               "ms_gemv": d["ms_gemv"], "algorithmic_bytes": d["bytes"],
                               "weights": "rotated over 5 device copies (679 MB) to defeat the Infinity Cache"})
@@ -277,6 +338,7 @@ def main():
                                f"W{wl.wbits}A{wl.abits} hblock={wl.hblock}, weights warm in HBM",
                    "global_batch": wl.M, "parallelism": "single GPU"},
         "frac_int8_peak": r["tops"] / PEAK_INT8_TOPS,
+        "batch_spread": r["batches"],
         "ms_prologue": r["ms_prologue"],
         "ms_gemm": r["ms_gemm"],
         "parity": r["parity"],
