@@ -10,10 +10,10 @@
 //   - MFMA: v_mfma_i32_32x32x32_i8 with the weight fragment (32 rows n) as the
 //     A operand and the token fragment (32 tokens m) as B; lane l holds token
 //     l % 32 of the result and rows n = 8 g + 4 (l / 32) + i in register 4 g + i.
-//     8-bit x 8-bit codes use v_mfma_i32_16x16x64_i8 instead (the MF16 form:
-//     16-row fragments, so no padded rows for a 144-row tile, and a higher
-//     sustained rate under the power limit); lane l then holds token l % 16
-//     and rows n = 4 (l / 16) + i.
+//     By default v_mfma_i32_16x16x64_i8 is used instead (the MF16 form: 16-row
+//     fragments, so no padded rows for a 144-row tile, and a higher sustained
+//     rate under the power limit); lane l then holds token l % 16 and rows
+//     n = 4 (l / 16) + i.
 //   - k advances in stages of 128 (256 with a 4-bit operand).  A stage of the
 //     two operand tiles is copied global -> LDS with global_load_lds_dwordx4 (no
 //     VGPR staging); NS stages live in an LDS ring, so NS-1 stages of loads are
@@ -99,11 +99,11 @@ struct Cfg {
     static constexpr int TN = BNC / 32;   // 32-row weight fragments per wave
     static constexpr int TN0 = (TN + 1) / 2;  // output fragments stored by the k-half 0 wave
     static constexpr int NLO = C / 4, NHI = (C + 3) / 4;
-    // MF16: v_mfma_i32_16x16x64_i8 instead of 32x32x32 (8-bit codes only): rows
-    // in fragments of 16, one 64-deep k step per wave per stage, TF16 token
-    // and TW16 row fragments per wave, weight fragments read D16 - 1 ahead
-    // through a ring of D16 registers (D16 divides TW16, so every stage starts
-    // at ring slot 0; at least 3, or 5 when a fragment feeds only two MFMAs)
+    // MF16: v_mfma_i32_16x16x64_i8 instead of 32x32x32: rows in fragments of
+    // 16, NSW16 64-deep k steps per wave per stage, TF16 token and TW16 row
+    // fragments per wave, weight fragments read D16 - 1 ahead through a ring
+    // of D16 registers (D16 divides TW16, so every step starts at ring slot 0;
+    // at least 3, or 5 when a fragment feeds only two MFMAs)
     static constexpr bool MF16 = MF16_;
     static constexpr int TF16 = BM / 32;
     static constexpr int TW16 = BNC / 16;
@@ -116,7 +116,7 @@ struct Cfg {
     static constexpr int D16 = ring16();
     static_assert(BM == 64 || BM == 128, "two waves of 32 or 64 tokens");
     static_assert(BNC % (MF16 ? 16 : 32) == 0 && BNC >= BNS, "computed rows in whole MFMA fragments");
-    static_assert(!MF16 || (ABITS == 8 && WBITS == 8 && KS == 128), "the 16x16x64 path takes 8-bit codes");
+    static constexpr int NSW16 = KS / 128;  // 64-deep steps per wave per stage (the k halves alternate)
     static_assert((BM * RA) % 1024 == 0 && (BNC * RW) % 1024 == 0, "whole 1 KB loads");
     static_assert(LDS <= 163840, "LDS ring exceeds 160 KiB");
     static_assert(NS >= 3, "the ring needs a slot being filled, one ready and one being read");
@@ -157,11 +157,13 @@ __device__ __forceinline__ int operand_offset(int lane, int j) {
     return 16 * slot_of<R>(rho, j) + 8 * h;                 // 16 k = 8 bytes
 }
 
-// The same for v_mfma_i32_16x16x64_i8 with 8-bit codes: lane l serves row
-// l % 16 of the fragment and k = 64 s + 16 (l / 16) + [0, 16) of 64-deep step s.
-template <int R>
+// The same for v_mfma_i32_16x16x64_i8: lane l serves row l % 16 of the
+// fragment and k = 64 s + 16 (l / 16) + [0, 16) of 64-deep step s.
+template <int BITS, int R>
 __device__ __forceinline__ int operand_offset16(int lane, int s) {
-    return 16 * slot_of<R>(lane & 15, 4 * s + (lane >> 4));
+    const int rho = lane & 15, q = lane >> 4;
+    if (BITS == 8) return 16 * slot_of<R>(rho, 4 * s + q);             // 16 k = 16 bytes
+    return 16 * slot_of<R>(rho, 2 * s + (q >> 1)) + 8 * (q & 1);        // 16 k = 8 bytes
 }
 
 template <int BITS, int PARTNER>
@@ -325,58 +327,80 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
     } else if constexpr (CF::MF16) {
         // ------------------------------------------- MFMA waves, 16x16x64 form
         // wave roles: tokens wm * BM/2 .. + BM/2 (TF16 fragments of 16), all BNC
-        // weight rows (TW16 fragments of 16), 64-deep k step kh of every stage.
-        // Weight fragment p of a stage is read while the MFMAs of fragment
-        // p - (D - 1) run; the reads that would start the next stage wait for
+        // weight rows (TW16 fragments of 16), the 64-deep k steps 2 i + kh of
+        // every stage.  The (step, weight fragment) units of a stage run in
+        // order; the unit D - 1 ahead is read while the current one's MFMAs
+        // run, and a step's token fragments are read with its first weight
+        // fragment.  The reads that would start the next stage first wait for
         // this wave's reads of the stage and for the barrier that publishes it.
-        constexpr int TF = CF::TF16, TW = CF::TW16, D = CF::D16;
+        // A half-deep last stage (4-bit operands, K % 256 = 128) has one step
+        // per wave and no barrier.
+        constexpr int TF = CF::TF16, TW = CF::TW16, D = CF::D16, NSW = CF::NSW16;
         const int wm = wave & 1;
         const int kh = wave >> 1;
-        const int offa = operand_offset16<CF::RA>(lane, kh) + wm * (CF::BM / 2) * CF::RA;
-        const int offw = operand_offset16<CF::RW>(lane, kh) + CF::CA * 1024;
+        int offa[NSW], offw[NSW];
+#pragma unroll
+        for (int i = 0; i < NSW; ++i) {
+            offa[i] = operand_offset16<ABITS, CF::RA>(lane, 2 * i + kh) + wm * (CF::BM / 2) * CF::RA;
+            offw[i] = operand_offset16<WBITS, CF::RW>(lane, 2 * i + kh) + CF::CA * 1024;
+        }
         v4i acc[TW][TF];
 #pragma unroll
         for (int n = 0; n < TW; ++n)
 #pragma unroll
             for (int f = 0; f < TF; ++f) acc[n][f] = v4i{0, 0, 0, 0};
         v4i fa[2][TF], ring[D];
-        auto read_a = [&](int s, int b) {
-            const uint8_t* base = lds + (s % CF::NS) * CF::STAGE + offa;
+        auto read_a = [&](int s, int i, int b) {
+            const uint8_t* base = lds + (s % CF::NS) * CF::STAGE + offa[i];
 #pragma unroll
-            for (int f = 0; f < TF; ++f)
-                fa[b][f] = frag_from_bytes(*reinterpret_cast<const uint4*>(base + f * 16 * CF::RA));
+            for (int f = 0; f < TF; ++f) fa[b][f] = operand_from_lds<ABITS, WBITS>(base + f * 16 * CF::RA);
         };
-        auto read_w = [&](int s, int n) {
-            return frag_from_bytes(
-                *reinterpret_cast<const uint4*>(lds + (s % CF::NS) * CF::STAGE + offw + n * 16 * CF::RW));
+        auto read_w = [&](int s, int i, int n) {
+            return operand_from_lds<WBITS, ABITS>(lds + (s % CF::NS) * CF::STAGE + offw[i] + n * 16 * CF::RW);
         };
         barrier_nofence();  // stage 0 published
-        read_a(0, 0);
+        read_a(0, 0, 0);
 #pragma unroll
-        for (int q = 0; q < D - 1; ++q) ring[q] = read_w(0, q);
-        auto stage16 = [&](int s, auto buf_tag) {
-            constexpr int B = decltype(buf_tag)::value;
-            const bool has_next = s + 1 < nk;
+        for (int q = 0; q < D - 1; ++q) ring[q] = read_w(0, 0, q);
+        // stage s; SP = the stage's parity (token-fragment buffer of step i is
+        // (SP * NSW + i) & 1); HALF: a half-deep last stage
+        auto stage16 = [&](int s, auto sp_tag, auto half_tag) {
+            constexpr int SP = decltype(sp_tag)::value;
+            constexpr bool kHalf = decltype(half_tag)::value;
+            constexpr int steps = kHalf ? 1 : NSW;
+            constexpr int units = steps * TW;
+            const bool has_next = !kHalf && s + 1 < nk;
 #pragma unroll
-            for (int n = 0; n < TW; ++n) {
-                const int q = n + D - 1;  // the fragment read in this iteration
-                if (q < TW) {
-                    ring[q % D] = read_w(s, q);
-                } else {
-                    if (q == TW) {
+            for (int t = 0; t < units; ++t) {
+                const int i = t / TW, n = t % TW;
+                const int q = t + D - 1;  // the unit read in this iteration
+                if (q < units) {
+                    if (q % TW == 0) read_a(s, q / TW, (SP * NSW + q / TW) & 1);
+                    ring[q % D] = read_w(s, q / TW, q % TW);
+                } else if (!kHalf) {
+                    if (q == units) {
                         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave is done with stage s
                         barrier_nofence();
-                        if (has_next) read_a(s + 1, B ^ 1);
+                        if (has_next) read_a(s + 1, 0, ((SP + 1) * NSW) & 1);
                     }
-                    if (has_next) ring[q % D] = read_w(s + 1, q - TW);
+                    if (has_next) ring[q % D] = read_w(s + 1, 0, q - units);
                 }
+                const int b = (SP * NSW + i) & 1;
 #pragma unroll
-                for (int f = 0; f < TF; ++f) acc[n][f] = mfma16x16x64(ring[n % D], fa[B][f], acc[n][f]);
+                for (int f = 0; f < TF; ++f) acc[n][f] = mfma16x16x64(ring[n % D], fa[b][f], acc[n][f]);
             }
         };
-        for (int s = 0; s < nk; s += 2) {
-            stage16(s, std::integral_constant<int, 0>{});
-            if (s + 1 < nk) stage16(s + 1, std::integral_constant<int, 1>{});
+        for (int s = 0; s < nfull; s += 2) {
+            stage16(s, std::integral_constant<int, 0>{}, std::false_type{});
+            if (s + 1 < nfull) stage16(s + 1, std::integral_constant<int, 1>{}, std::false_type{});
+        }
+        if constexpr (NSW > 1) {  // only 4-bit operands have half-deep stages
+            if (half_last) {
+                if (nfull % 2 == 0)
+                    stage16(nfull, std::integral_constant<int, 0>{}, std::true_type{});
+                else
+                    stage16(nfull, std::integral_constant<int, 1>{}, std::true_type{});
+            }
         }
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's ring reads are done
         load_epilogue_operands();
@@ -586,12 +610,12 @@ constexpr int ring_depth() {
     return n > 8 ? 8 : n;
 }
 
-// MFMA form of 8-bit x 8-bit GEMMs: v_mfma_i32_16x16x64_i8 (rows in fragments
-// of 16, so a 144-row tile computes no padding rows) unless the test hook
-// FQ_GEMM_MFMA=32 asks for v_mfma_i32_32x32x32_i8.  The 16x16x64 form measured
-// 6-7 % faster on the qkv and down layers (22.8 against 24.6 us, 73.9 against
-// 79.1 us), also where no rows are padded: with random operands it sustains a
-// higher rate under the power limit (3.4-3.6 against 3.2-3.3 POP/s).
+// MFMA form: v_mfma_i32_16x16x64_i8 (rows in fragments of 16, so a 144-row
+// tile computes no padding rows) unless the test hook FQ_GEMM_MFMA=32 asks for
+// v_mfma_i32_32x32x32_i8.  The 16x16x64 form measured 6-7 % faster on the
+// W8A8 qkv and down layers (22.8 against 24.6 us, 73.9 against 79.1 us), also
+// where no rows are padded: with random operands it sustains a higher rate
+// under the power limit (3.4-3.6 against 3.2-3.3 POP/s).
 int mfma_form() {
     const char* e = std::getenv("FQ_GEMM_MFMA");
     return e ? std::atoi(e) : 16;
@@ -601,12 +625,18 @@ template <int ABITS, int WBITS, int BM, int BNS>
 hipError_t launch_shape(const GemmArgs& g, hipStream_t st) {
     constexpr int bnc = (BNS + 31) / 32 * 32;
     constexpr int ns = ring_depth<ABITS, WBITS, BM, bnc>();
-    if constexpr (ABITS == 8 && WBITS == 8) {
-        if (mfma_form() == 16) {
-            constexpr int bnc16 = (BNS + 15) / 16 * 16;
-            constexpr int ns16 = ring_depth<ABITS, WBITS, BM, bnc16>();
-            return launch_cfg<ABITS, WBITS, Cfg<ABITS, WBITS, BM, BNS, bnc16, ns16, 128, true>>(g, st);
-        }
+    constexpr int bnc16 = (BNS + 15) / 16 * 16;
+    constexpr int ns16 = ring_depth<ABITS, WBITS, BM, bnc16>();
+    // With a 4-bit operand the 16x16x64 form runs two steps per stage and
+    // unpacks the nibbles of every weight fragment.  It pays only where each
+    // unpacked fragment feeds four MFMAs (128-token tiles) and the 24
+    // accumulator fragments still fit without spilling: of the eight tiles
+    // that is 128 x 96 (W4A4 down projection 57.1 against 61.8 us, gate+up
+    // 108.7 against 120.4); with 64-token tiles it was slower (58.9 against
+    // 49.7 us), so the other tiles keep the 32x32x32 form for 4-bit codes.
+    constexpr bool mf16 = ns16 >= 3 && ((ABITS == 8 && WBITS == 8) || (BM == 128 && (bnc16 / 16) * 4 <= 24));
+    if constexpr (mf16) {
+        if (mfma_form() == 16) return launch_cfg<ABITS, WBITS, Cfg<ABITS, WBITS, BM, BNS, bnc16, ns16, 128, true>>(g, st);
     }
     if constexpr (ns >= 3) {
         return launch_cfg<ABITS, WBITS, Cfg<ABITS, WBITS, BM, BNS, bnc, ns>>(g, st);
