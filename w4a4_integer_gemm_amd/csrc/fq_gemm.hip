@@ -406,30 +406,43 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
         load_epilogue_operands();
         barrier_nofence();                   // E1: the ring is idle
 
-        // k-half 1 partial sums into X, then k-half 0 adds its own.  Lane l
-        // holds token wm BM/2 + 16 f + l % 16 and rows 16 n + 4 (l / 16) + [0, 4).
+        // The two k halves meet in X: the k-half 0 wave finishes row fragments
+        // n < TWH and the k-half 1 wave the rest.  Each first stores the
+        // fragments the other finishes, then adds the other's partial sums to
+        // its own and stores the total (half the serial LDS work of one wave
+        // doing all the adds).  Lane l holds token wm BM/2 + 16 f + l % 16 and
+        // rows 16 n + 4 (l / 16) + [0, 4).
         int32_t* X = reinterpret_cast<int32_t*>(lds);
         constexpr int XS = acc_stride<CF>();
+        constexpr int TWH = (TW + 1) / 2;
         auto xrow = [&](int f, int n) {
             const int m = wm * (CF::BM / 2) + 16 * f + (lane & 15);
             return reinterpret_cast<v4i*>(X + m * XS + 16 * n + 4 * (lane >> 4));
         };
-        if (kh == 1) {
+        // (one code path per k half, so that which fragments a wave owns is
+        // known at compile time)
+        auto exchange = [&](auto kh_tag) {
+            constexpr int KH = decltype(kh_tag)::value;
+            constexpr int own_lo = KH == 0 ? 0 : TWH, own_hi = KH == 0 ? TWH : TW;
 #pragma unroll
             for (int n = 0; n < TW; ++n)
+                if (n < own_lo || n >= own_hi) {
 #pragma unroll
-                for (int f = 0; f < TF; ++f) *xrow(f, n) = acc[n][f];
-        }
-        barrier_nofence();  // E2
-        if (kh == 0) {
+                    for (int f = 0; f < TF; ++f) *xrow(f, n) = acc[n][f];
+                }
+            barrier_nofence();  // E2
 #pragma unroll
-            for (int n = 0; n < TW; ++n)
+            for (int n = own_lo; n < own_hi; ++n)
 #pragma unroll
                 for (int f = 0; f < TF; ++f) {
                     v4i* p = xrow(f, n);
                     *p = acc[n][f] + *p;
                 }
-        }
+        };
+        if (kh == 0)
+            exchange(std::integral_constant<int, 0>{});
+        else
+            exchange(std::integral_constant<int, 1>{});
         barrier_nofence();  // E3
     } else {
         // ---------------------------------------------------------- MFMA waves
