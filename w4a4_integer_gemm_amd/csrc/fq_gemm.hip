@@ -334,7 +334,11 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
         // fragment.  The reads that would start the next stage first wait for
         // this wave's reads of the stage and for the barrier that publishes it.
         // A half-deep last stage (4-bit operands, K % 256 = 128) has one step
-        // per wave and no barrier.
+        // per wave and no barrier.  The last stage reads "next stage" operands
+        // from slot (s + 1) % NS too and never uses them: with no condition on
+        // those reads the loop is straight-line code, whose LDS waits the
+        // compiler counts exactly (a conditional read made it wait for every
+        // read in flight, the one just issued included, at each stage start).
         constexpr int TF = CF::TF16, TW = CF::TW16, D = CF::D16, NSW = CF::NSW16;
         const int wm = wave & 1;
         const int kh = wave >> 1;
@@ -362,6 +366,11 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
         read_a(0, 0, 0);
 #pragma unroll
         for (int q = 0; q < D - 1; ++q) ring[q] = read_w(0, 0, q);
+        // with nothing in flight on entry, the compiler's LDS wait at the top of
+        // the stage loop counts the reads of the loop's back edge alone (a read
+        // still in flight from here made it wait for all of them)
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_sched_barrier(0);
         // stage s; SP = the stage's parity (token-fragment buffer of step i is
         // (SP * NSW + i) & 1); HALF: a half-deep last stage
         auto stage16 = [&](int s, auto sp_tag, auto half_tag) {
@@ -369,37 +378,60 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
             constexpr bool kHalf = decltype(half_tag)::value;
             constexpr int steps = kHalf ? 1 : NSW;
             constexpr int units = steps * TW;
-            const bool has_next = !kHalf && s + 1 < nk;
 #pragma unroll
             for (int t = 0; t < units; ++t) {
                 const int i = t / TW, n = t % TW;
                 const int q = t + D - 1;  // the unit read in this iteration
+                const int b = (SP * NSW + i) & 1;
+                auto mfmas = [&]() {
+#pragma unroll
+                    for (int f = 0; f < TF; ++f) acc[n][f] = mfma16x16x64(ring[n % D], fa[b][f], acc[n][f]);
+                };
+                // the scheduling barriers keep this order: left to itself the
+                // compiler moved reads next to their first use
                 if (q < units) {
                     if (q % TW == 0) read_a(s, q / TW, (SP * NSW + q / TW) & 1);
                     ring[q % D] = read_w(s, q / TW, q % TW);
+                    __builtin_amdgcn_sched_barrier(0);
+                    mfmas();
                 } else if (!kHalf) {
                     if (q == units) {
+                        // the unit's MFMAs go first so that the wait below finds
+                        // the stage's last read landed
+                        mfmas();
+                        __builtin_amdgcn_sched_barrier(0);
                         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave is done with stage s
                         barrier_nofence();
-                        if (has_next) read_a(s + 1, 0, ((SP + 1) * NSW) & 1);
+                        read_a(s + 1, 0, ((SP + 1) * NSW) & 1);
+                        ring[q % D] = read_w(s + 1, 0, 0);
+                    } else {
+                        ring[q % D] = read_w(s + 1, 0, q - units);
+                        __builtin_amdgcn_sched_barrier(0);
+                        mfmas();
                     }
-                    if (has_next) ring[q % D] = read_w(s + 1, 0, q - units);
+                } else {
+                    mfmas();
                 }
-                const int b = (SP * NSW + i) & 1;
-#pragma unroll
-                for (int f = 0; f < TF; ++f) acc[n][f] = mfma16x16x64(ring[n % D], fa[b][f], acc[n][f]);
+                __builtin_amdgcn_sched_barrier(0);
             }
         };
-        for (int s = 0; s < nfull; s += 2) {
+        // stages in unconditional pairs (a conditional second stage inside the
+        // loop made the compiler copy the accumulators at every iteration to
+        // reconcile the two paths), then an odd last full stage, then the
+        // half-deep stage of 4-bit operands
+        int s = 0;
+        for (; s + 1 < nfull; s += 2) {
             stage16(s, std::integral_constant<int, 0>{}, std::false_type{});
-            if (s + 1 < nfull) stage16(s + 1, std::integral_constant<int, 1>{}, std::false_type{});
+            stage16(s + 1, std::integral_constant<int, 1>{}, std::false_type{});
         }
+        const bool odd = s < nfull;
+        if (odd) stage16(s, std::integral_constant<int, 0>{}, std::false_type{});
         if constexpr (NSW > 1) {  // only 4-bit operands have half-deep stages
             if (half_last) {
-                if (nfull % 2 == 0)
-                    stage16(nfull, std::integral_constant<int, 0>{}, std::true_type{});
-                else
+                if (odd)
                     stage16(nfull, std::integral_constant<int, 1>{}, std::true_type{});
+                else
+                    stage16(nfull, std::integral_constant<int, 0>{}, std::true_type{});
             }
         }
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's ring reads are done
