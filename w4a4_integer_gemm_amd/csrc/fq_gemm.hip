@@ -73,6 +73,21 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | 0x70 | 0xF00 | ((N >> 4) << 14));
 }
 
+// vmcnt(k * NHI) for a k known only at run time (0 <= k < 8, k * NHI < 64)
+template <int NHI>
+__device__ __forceinline__ void wait_stages_in_flight(int k) {
+    switch (k) {
+        case 0: wait_vmcnt<0>(); break;
+        case 1: if constexpr (1 * NHI < 64) { wait_vmcnt<1 * NHI>(); break; } [[fallthrough]];
+        case 2: if constexpr (2 * NHI < 64) { wait_vmcnt<2 * NHI>(); break; } [[fallthrough]];
+        case 3: if constexpr (3 * NHI < 64) { wait_vmcnt<3 * NHI>(); break; } [[fallthrough]];
+        case 4: if constexpr (4 * NHI < 64) { wait_vmcnt<4 * NHI>(); break; } [[fallthrough]];
+        case 5: if constexpr (5 * NHI < 64) { wait_vmcnt<5 * NHI>(); break; } [[fallthrough]];
+        case 6: if constexpr (6 * NHI < 64) { wait_vmcnt<6 * NHI>(); break; } [[fallthrough]];
+        default: wait_vmcnt<0>(); break;
+    }
+}
+
 // Workgroup barrier without a memory fence (the LDS-DMA waits are explicit);
 // the empty asm statements keep the compiler from moving LDS accesses across it.
 __device__ __forceinline__ void barrier_nofence() {
@@ -312,11 +327,19 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
         wait_vmcnt<(CF::NS - 2) * CF::NHI>();
         barrier_nofence();
         // After barrier s-1 every MFMA wave is done with stage s-1, whose slot
-        // takes stage s + NS - 1 (past the end of K: the last stage again, never
-        // read).  Barrier s publishes stage s + 1.
+        // takes stage s + NS - 1 while that is a stage of K.  Barrier s
+        // publishes stage s + 1: the wait lets the stages issued after it stay
+        // in flight (NS - 2 of them, fewer in the last iterations, which issue
+        // nothing; the epilogue's loads then do not queue behind copies).
+        int issued = CF::NS - 1;  // stage copies issued so far
         for (int s = 0; s < nfull; ++s) {
-            load_stage(s + CF::NS - 1 < nk ? s + CF::NS - 1 : nk - 1, (s + CF::NS - 1) % CF::NS);
-            wait_vmcnt<(CF::NS - 2) * CF::NHI>();
+            if (s + CF::NS - 1 < nk) {
+                load_stage(s + CF::NS - 1, (s + CF::NS - 1) % CF::NS);
+                ++issued;
+                wait_vmcnt<(CF::NS - 2) * CF::NHI>();
+            } else {
+                wait_stages_in_flight<CF::NHI>(issued - (s + 2));
+            }
             barrier_nofence();
         }
         wait_vmcnt<0>();      // every ring load has landed
