@@ -181,12 +181,34 @@ __device__ __forceinline__ int operand_offset16(int lane, int s) {
     return 16 * slot_of<R>(rho, 2 * s + (q >> 1)) + 8 * (q & 1);        // 16 k = 8 bytes
 }
 
+// One lane's operand chunk as read from LDS (`raw`: 8 bytes of nibbles or 16
+// code bytes) and as the MFMA takes it (`expand`).  The MFMA waves read raw
+// chunks ahead and expand them only where they are used: expanding next to the
+// read would make the wave wait for the read there.  8-bit codes facing 8-bit
+// codes need no expansion (kIdentity).
 template <int BITS, int PARTNER>
-__device__ __forceinline__ v4i operand_from_lds(const uint8_t* p) {
-    if (BITS == 4) return frag_from_nibbles(*reinterpret_cast<const uint2*>(p));
-    const uint4 v = *reinterpret_cast<const uint4*>(p);
-    return PARTNER == 4 ? frag_from_bytes_nibble_order(v) : frag_from_bytes(v);
-}
+struct LdsOperand;
+template <int PARTNER>
+struct LdsOperand<4, PARTNER> {
+    typedef uint2 raw;
+    static constexpr bool kIdentity = false;
+    __device__ __forceinline__ static raw load(const uint8_t* p) { return *reinterpret_cast<const uint2*>(p); }
+    __device__ __forceinline__ static v4i expand(raw r) { return frag_from_nibbles(r); }
+};
+template <>
+struct LdsOperand<8, 4> {
+    typedef uint4 raw;
+    static constexpr bool kIdentity = false;
+    __device__ __forceinline__ static raw load(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
+    __device__ __forceinline__ static v4i expand(raw r) { return frag_from_bytes_nibble_order(r); }
+};
+template <>
+struct LdsOperand<8, 8> {
+    typedef v4i raw;
+    static constexpr bool kIdentity = true;
+    __device__ __forceinline__ static raw load(const uint8_t* p) { return *reinterpret_cast<const v4i*>(p); }
+    __device__ __forceinline__ static v4i expand(raw r) { return r; }
+};
 
 // global source of 1 KB load q of an operand tile for `lane`: row rho of the
 // tile and 16-byte column kc, the inverse of slot_of
@@ -376,14 +398,18 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
         for (int n = 0; n < TW; ++n)
 #pragma unroll
             for (int f = 0; f < TF; ++f) acc[n][f] = v4i{0, 0, 0, 0};
-        v4i fa[2][TF], ring[D];
+        typedef LdsOperand<ABITS, WBITS> OpA;
+        typedef LdsOperand<WBITS, ABITS> OpW;
+        typename OpA::raw fa_raw[2][TF];  // token fragments of two steps, as read
+        typename OpW::raw ring[D];         // weight fragments, as read
+        v4i fa[TF];                        // the current step's token fragments, expanded
         auto read_a = [&](int s, int i, int b) {
             const uint8_t* base = lds + (s % CF::NS) * CF::STAGE + offa[i];
 #pragma unroll
-            for (int f = 0; f < TF; ++f) fa[b][f] = operand_from_lds<ABITS, WBITS>(base + f * 16 * CF::RA);
+            for (int f = 0; f < TF; ++f) fa_raw[b][f] = OpA::load(base + f * 16 * CF::RA);
         };
         auto read_w = [&](int s, int i, int n) {
-            return operand_from_lds<WBITS, ABITS>(lds + (s % CF::NS) * CF::STAGE + offw[i] + n * 16 * CF::RW);
+            return OpW::load(lds + (s % CF::NS) * CF::STAGE + offw[i] + n * 16 * CF::RW);
         };
         barrier_nofence();  // stage 0 published
         read_a(0, 0, 0);
@@ -407,8 +433,16 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
                 const int q = t + D - 1;  // the unit read in this iteration
                 const int b = (SP * NSW + i) & 1;
                 auto mfmas = [&]() {
+                    if constexpr (!OpA::kIdentity) {
+                        if (n == 0) {  // a step's first unit expands its token fragments
 #pragma unroll
-                    for (int f = 0; f < TF; ++f) acc[n][f] = mfma16x16x64(ring[n % D], fa[b][f], acc[n][f]);
+                            for (int f = 0; f < TF; ++f) fa[f] = OpA::expand(fa_raw[b][f]);
+                        }
+                    }
+                    const v4i w = OpW::expand(ring[n % D]);
+#pragma unroll
+                    for (int f = 0; f < TF; ++f)
+                        acc[n][f] = mfma16x16x64(w, OpA::kIdentity ? OpA::expand(fa_raw[b][f]) : fa[f], acc[n][f]);
                 };
                 // the scheduling barriers keep this order: left to itself the
                 // compiler moved reads next to their first use
@@ -518,23 +552,25 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
 #pragma unroll
             for (int f = 0; f < CF::TMF; ++f) acc[i][f] = v16i{};
 
-        v4i fa[2][CF::TMF], fw[2][CF::TN];
+        typedef LdsOperand<ABITS, WBITS> OpA;
+        typedef LdsOperand<WBITS, ABITS> OpW;
+        typename OpA::raw fa[2][CF::TMF];  // two steps' operands, as read
+        typename OpW::raw fw[2][CF::TN];
         auto read_frags = [&](int s, int i, int buf) {
             const uint8_t* base = lds + (s % CF::NS) * CF::STAGE;
 #pragma unroll
-            for (int f = 0; f < CF::TMF; ++f)
-                fa[buf][f] = operand_from_lds<ABITS, WBITS>(base + offa[i] + f * 32 * CF::RA);
+            for (int f = 0; f < CF::TMF; ++f) fa[buf][f] = OpA::load(base + offa[i] + f * 32 * CF::RA);
 #pragma unroll
-            for (int n = 0; n < CF::TN; ++n)
-                fw[buf][n] = operand_from_lds<WBITS, ABITS>(base + offw[i] + n * 32 * CF::RW);
+            for (int n = 0; n < CF::TN; ++n) fw[buf][n] = OpW::load(base + offw[i] + n * 32 * CF::RW);
         };
 
         barrier_nofence();  // stage 0 published
         read_frags(0, 0, 0);
 
         // One k stage.  In each step the first TMF MFMAs run on operands read
-        // one step earlier; then the next step's operands are read from LDS
-        // (their latency hides behind the remaining MFMAs).  Before the last
+        // one step earlier (expanded at the step's start); then the next step's
+        // operands are read from LDS (their latency hides behind the remaining
+        // MFMAs).  Before the last
         // step this wave's reads of the stage are waited for and the barrier
         // both frees the stage's slot and publishes the next stage.  A
         // half-deep last stage (FULL = false) runs its first NSTEP/2 steps and
@@ -546,8 +582,12 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
 #pragma unroll
             for (int j = 0; j < kSteps; ++j) {
                 const int cur = j & 1;
+                v4i xa[CF::TMF];  // this step's token fragments, expanded
 #pragma unroll
-                for (int f = 0; f < CF::TMF; ++f) acc[0][f] = mfma32x32x32(fw[cur][0], fa[cur][f], acc[0][f]);
+                for (int f = 0; f < CF::TMF; ++f) xa[f] = OpA::expand(fa[cur][f]);
+                const v4i w0 = OpW::expand(fw[cur][0]);
+#pragma unroll
+                for (int f = 0; f < CF::TMF; ++f) acc[0][f] = mfma32x32x32(w0, xa[f], acc[0][f]);
                 __builtin_amdgcn_sched_barrier(0);
                 if (j + 1 < kSteps) {
                     read_frags(s, j + 1, cur ^ 1);
@@ -558,9 +598,11 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
                 }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int n = 1; n < CF::TN; ++n)
+                for (int n = 1; n < CF::TN; ++n) {
+                    const v4i w = OpW::expand(fw[cur][n]);
 #pragma unroll
-                    for (int f = 0; f < CF::TMF; ++f) acc[n][f] = mfma32x32x32(fw[cur][n], fa[cur][f], acc[n][f]);
+                    for (int f = 0; f < CF::TMF; ++f) acc[n][f] = mfma32x32x32(w, xa[f], acc[n][f]);
+                }
             }
         };
         for (int s = 0; s < nfull; ++s) stage(s, std::true_type{});
