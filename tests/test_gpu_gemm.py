@@ -54,7 +54,7 @@ SHAPES = [
     (300, 1000, 2048), (816, 264, 1024),
 ]
 
-TILES = ["128x128", "128x144", "128x112", "128x96", "64x128", "64x224", "64x256", "64x288"]
+TILES = ["128x128", "128x144", "128x112", "128x96", "64x128", "64x224", "64x256", "64x288", "64x128x2"]
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "M{}_N{}_K{}".format(*s))
@@ -113,6 +113,39 @@ def test_gemm_every_tile_shape_32x32x32_form(tile, monkeypatch):
     monkeypatch.setenv("FQ_GEMM_MFMA", "32")
     log(f"gemm tile {tile} 32x32x32 form")
     _tile_case(tile, (8, 8))
+
+
+@pytest.mark.parametrize("bits", [(8, 8), (4, 4)], ids=lambda b: "A{}W{}".format(*b))
+def test_gemm_two_workgroups_per_cu_many_tiles(bits, monkeypatch):
+    """The two-per-CU 64 x 128 tile on 2048 tiles (two workgroups share each
+    CU, several waves of them): every int32 sum equals the 128 x 128 tile's
+    (the sums do not depend on the tiling), and sampled token rows equal the
+    oracle's exactly.  The samples include rows 32..63 of several tiles, whose
+    partial sums pass between waves through LDS in the epilogue."""
+    from w4a4_integer_gemm_amd import fq_gemm
+    M, N, K = 1024, 8192, 1024
+    abits, wbits = bits
+    log(f"gemm two per CU M={M} N={N} K={K} A{abits}W{wbits}")
+    rng = np.random.default_rng(11 + abits)
+    ca, cw = rand_codes(rng, M, K, abits), rand_codes(rng, N, K, wbits)
+    sa = rng.uniform(0.001, 0.05, M).astype(np.float32)
+    sw = rng.uniform(0.0001, 0.002, N).astype(np.float32)
+    d_ca, d_cw, d_sa, d_sw = dev(ca), dev(cw), dev(sa), dev(sw)
+    out = {}
+    for tile in ("64x128x2", "128x128"):
+        monkeypatch.setenv("FQ_GEMM_TILE", tile)
+        y = dev(np.zeros((M, N), np.uint16))
+        acc = dev(np.zeros((M, N), np.int32))
+        fq_gemm(d_ca, d_sa, M, abits, d_cw, d_sw, N, K, wbits, None, None, N, y, N, acc)
+        out[tile] = (host(acc), host(y, np.uint16))
+    acc2, y2 = out["64x128x2"]
+    assert np.array_equal(acc2, out["128x128"][0]), f"{np.count_nonzero(acc2 != out['128x128'][0])} sums differ"
+    rows = sorted(set([0, M - 1] + [64 * t + r for t in (0, 7, 15) for r in (0, 32, 33, 35, 48, 51, 63)]
+                      + rng.choice(M, 16, replace=False).tolist()))
+    acc_ref = oracle.gemm_i32(ca[rows], abits, cw, wbits, K)
+    assert np.array_equal(acc2[rows], acc_ref)
+    _, yf = oracle.epilogue(acc_ref, sa[rows], sw, want_f64=True)
+    assert_y_elementwise(y2[rows], yf, acc_ref, sa[rows], sw, what="two per CU")
 
 
 GEMV_SHAPES = [

@@ -90,14 +90,27 @@ __device__ __forceinline__ void wait_stages_in_flight(int k) {
 
 // Workgroup barrier without a memory fence (the LDS-DMA waits are explicit);
 // the empty asm statements keep the compiler from moving LDS accesses across it.
+// On gfx950 s_barrier does not wait for the wave's own LDS accesses, and the
+// compiler adds no wait before it either: a wave whose LDS writes other waves
+// read past the barrier uses barrier_lds.
 __device__ __forceinline__ void barrier_nofence() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 }
+__device__ __forceinline__ void barrier_lds() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes have landed
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
 
-template <int ABITS, int WBITS, int BM_, int BNS_, int BNC_, int NS_, int KS8 = 128, bool MF16_ = false>
+template <int ABITS, int WBITS, int BM_, int BNS_, int BNC_, int NS_, int KS8 = 128, bool MF16_ = false,
+          bool TWO_ = false>
 struct Cfg {
+    // TWO: two workgroups share a CU (at most 80 KiB of LDS and 128 VGPRs
+    // each), so that one's fill and epilogue overlap the other's k loop
+    static constexpr bool TWO = TWO_;
     // BM tokens x BNS stored weight rows per tile; BNC >= BNS rows are computed
     // (a multiple of 32: the MFMA's row count); rows past BNS belong to the next
     // tile and are discarded.
@@ -133,7 +146,7 @@ struct Cfg {
     static_assert(BNC % (MF16 ? 16 : 32) == 0 && BNC >= BNS, "computed rows in whole MFMA fragments");
     static constexpr int NSW16 = KS / 128;  // 64-deep steps per wave per stage (the k halves alternate)
     static_assert((BM * RA) % 1024 == 0 && (BNC * RW) % 1024 == 0, "whole 1 KB loads");
-    static_assert(LDS <= 163840, "LDS ring exceeds 160 KiB");
+    static_assert(LDS <= (TWO ? 81920 : 163840), "LDS ring exceeds the workgroup's share of the CU");
     static_assert(NS >= 3, "the ring needs a slot being filled, one ready and one being read");
     static_assert((NS - 2) * NHI < 64, "vmcnt range");
     static_assert(MF16 || LDS >= 2 * TMF * TN * 4096, "the split-k exchange reuses the ring");
@@ -229,7 +242,7 @@ constexpr int acc_stride() {
 }
 
 template <int ABITS, int WBITS, class CF>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m, int tiles_n) {
+__device__ __forceinline__ void gemm_body(const GemmArgs& g, int tiles_m, int tiles_n) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[CF::LDS];
     static_assert(CF::BM * acc_stride<CF>() * 4 <= CF::LDS, "the epilogue tile reuses the ring");
 
@@ -519,7 +532,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
 #pragma unroll
                     for (int f = 0; f < TF; ++f) *xrow(f, n) = acc[n][f];
                 }
-            barrier_nofence();  // E2
+            barrier_lds();  // E2
 #pragma unroll
             for (int n = own_lo; n < own_hi; ++n)
 #pragma unroll
@@ -532,7 +545,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
             exchange(std::integral_constant<int, 0>{});
         else
             exchange(std::integral_constant<int, 1>{});
-        barrier_nofence();  // E3
+        barrier_lds();  // E3
     } else {
         // ---------------------------------------------------------- MFMA waves
         // wave roles: tokens wm * BM/2 .. + BM/2 (TMF fragments of 32), all BNC
@@ -631,7 +644,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
                         *xrow(f, n, q) = v4i{acc[n][f][4 * q], acc[n][f][4 * q + 1], acc[n][f][4 * q + 2],
                                              acc[n][f][4 * q + 3]};
         }
-        barrier_nofence();  // E2
+        barrier_lds();  // E2
         if (kh == 0) {
 #pragma unroll
             for (int n = 0; n < CF::TN; ++n)
@@ -645,7 +658,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
                                  acc[n][f][4 * q + 3] + v[3]};
                     }
         }
-        barrier_nofence();  // E3
+        barrier_lds();  // E3
     }
 
     // ---------------------------------------------------------------- epilogue
@@ -695,21 +708,39 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
 }
 
 template <int ABITS, int WBITS, class CF>
+__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m, int tiles_n) {
+    gemm_body<ABITS, WBITS, CF>(g, tiles_m, tiles_n);
+}
+
+// The same kernel held to 128 VGPRs per wave, so that two workgroups fit a CU.
+template <int ABITS, int WBITS, class CF>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void gemm_kernel_x2(GemmArgs g,
+                                                                                                  int tiles_m,
+                                                                                                  int tiles_n) {
+    gemm_body<ABITS, WBITS, CF>(g, tiles_m, tiles_n);
+}
+
+template <int ABITS, int WBITS, class CF>
 hipError_t launch_cfg(const GemmArgs& g, hipStream_t st) {
     const int tiles_m = (g.M + CF::BM - 1) / CF::BM;
     const int tiles_n = (g.N + CF::BNS - 1) / CF::BNS;
-    hipLaunchKernelGGL((gemm_kernel<ABITS, WBITS, CF>), dim3(tiles_m * tiles_n), dim3(kThreads), 0, st, g, tiles_m,
-                       tiles_n);
+    if constexpr (CF::TWO)
+        hipLaunchKernelGGL((gemm_kernel_x2<ABITS, WBITS, CF>), dim3(tiles_m * tiles_n), dim3(kThreads), 0, st, g,
+                           tiles_m, tiles_n);
+    else
+        hipLaunchKernelGGL((gemm_kernel<ABITS, WBITS, CF>), dim3(tiles_m * tiles_n), dim3(kThreads), 0, st, g,
+                           tiles_m, tiles_n);
     return hipGetLastError();
 }
 
 // Tile shapes: tokens x stored weight rows (computed rows rounded up to 32).
-enum TileId { T128x128 = 0, T128x144, T128x112, T128x96, T64x128, T64x224, T64x256, T64x288, kNumTiles };
+// 64x128x2: the 64 x 128 tile with a 3-stage ring, two workgroups per CU.
+enum TileId { T128x128 = 0, T128x144, T128x112, T128x96, T64x128, T64x224, T64x256, T64x288, T64x128x2, kNumTiles };
 
-const char* const kTileNames[kNumTiles] = {"128x128", "128x144", "128x112", "128x96",
-                                           "64x128",  "64x224",  "64x256",  "64x288"};
-const int kTileBM[kNumTiles] = {128, 128, 128, 128, 64, 64, 64, 64};
-const int kTileBN[kNumTiles] = {128, 144, 112, 96, 128, 224, 256, 288};
+const char* const kTileNames[kNumTiles] = {"128x128", "128x144", "128x112", "128x96",  "64x128",
+                                           "64x224",  "64x256",  "64x288",  "64x128x2"};
+const int kTileBM[kNumTiles] = {128, 128, 128, 128, 64, 64, 64, 64, 64};
+const int kTileBN[kNumTiles] = {128, 144, 112, 96, 128, 224, 256, 288, 128};
 
 // Pipeline depth: as many stages as fit in 160 KiB of LDS, at most 8.
 template <int ABITS, int WBITS, int BM, int BNC, int KS8 = 128>
@@ -731,12 +762,12 @@ int mfma_form() {
     return e ? std::atoi(e) : 16;
 }
 
-template <int ABITS, int WBITS, int BM, int BNS>
+template <int ABITS, int WBITS, int BM, int BNS, bool TWO = false>
 hipError_t launch_shape(const GemmArgs& g, hipStream_t st) {
     constexpr int bnc = (BNS + 31) / 32 * 32;
-    constexpr int ns = ring_depth<ABITS, WBITS, BM, bnc>();
+    constexpr int ns = TWO ? 3 : ring_depth<ABITS, WBITS, BM, bnc>();
     constexpr int bnc16 = (BNS + 15) / 16 * 16;
-    constexpr int ns16 = ring_depth<ABITS, WBITS, BM, bnc16>();
+    constexpr int ns16 = TWO ? 3 : ring_depth<ABITS, WBITS, BM, bnc16>();
     // With a 4-bit operand the 16x16x64 form runs two steps per stage and
     // unpacks the nibbles of every weight fragment.  It pays only where each
     // unpacked fragment feeds four MFMAs (128-token tiles) and the 24
@@ -746,10 +777,11 @@ hipError_t launch_shape(const GemmArgs& g, hipStream_t st) {
     // 49.7 us), so the other tiles keep the 32x32x32 form for 4-bit codes.
     constexpr bool mf16 = ns16 >= 3 && ((ABITS == 8 && WBITS == 8) || (BM == 128 && (bnc16 / 16) * 4 <= 24));
     if constexpr (mf16) {
-        if (mfma_form() == 16) return launch_cfg<ABITS, WBITS, Cfg<ABITS, WBITS, BM, BNS, bnc16, ns16, 128, true>>(g, st);
+        if (mfma_form() == 16)
+            return launch_cfg<ABITS, WBITS, Cfg<ABITS, WBITS, BM, BNS, bnc16, ns16, 128, true, TWO>>(g, st);
     }
     if constexpr (ns >= 3) {
-        return launch_cfg<ABITS, WBITS, Cfg<ABITS, WBITS, BM, BNS, bnc, ns>>(g, st);
+        return launch_cfg<ABITS, WBITS, Cfg<ABITS, WBITS, BM, BNS, bnc, ns, 128, false, TWO>>(g, st);
     } else {
         // this operand mix does not fit three stages of this tile: use 128 x 128
         return launch_cfg<ABITS, WBITS, Cfg<ABITS, WBITS, 128, 128, 128, ring_depth<ABITS, WBITS, 128, 128>()>>(g,
@@ -774,6 +806,11 @@ hipError_t launch_tile(int tile, const GemmArgs& g, hipStream_t st) {
             return launch_shape<ABITS, WBITS, 64, 256>(g, st);
         case T64x288:
             return launch_shape<ABITS, WBITS, 64, 288>(g, st);
+        case T64x128x2:  // (mixed 8-bit/4-bit codes: three stages do not fit in 80 KiB)
+            if constexpr (ABITS == WBITS)
+                return launch_shape<ABITS, WBITS, 64, 128, true>(g, st);
+            else
+                return launch_shape<ABITS, WBITS, 64, 128>(g, st);
         case T128x128:
         default:
             return launch_shape<ABITS, WBITS, 128, 128>(g, st);
@@ -789,17 +826,24 @@ hipError_t launch_tile(int tile, const GemmArgs& g, hipStream_t st) {
 // 816-token prefill layer: 128 x 144 for QKV (N = 4608, 256 tiles; 22.3 us
 // against 23.5 for 64 x 288), 128 x 112 for the W8A8 down projection (N =
 // 3584, 256 tiles; 69.2 us against 70.7 for 64 x 224 and 78.0 for 128 x 128,
-// which leaves 32 CUs idle), 128 x 128 for a W4A4 gate+up (N = 32768) and
-// 64 x 128 for its down projection (N = 2048).
-int choose_tile(int M, int N, int frag_rows) {
+// which leaves 32 CUs idle) and 64 x 128 for the W4A4 down projection (N =
+// 2048, 208 tiles).  The two-per-CU 64 x 128 tile takes 512 workgroups per
+// wave; where there are more tiles than CUs it hides one workgroup's fill and
+// epilogue behind the other's k loop.  With 4-bit codes that made it the
+// fastest tile for the W4A4 gate+up (N = 32768, 3328 tiles: 70 us against 91
+// for 128 x 128) and for M = N = K = 4096 (78 against 84), hence 1.15; with
+// 8-bit codes it only matched the 128-token tiles (0.95).
+int choose_tile(int M, int N, int frag_rows, bool four_bit, bool two_per_cu) {
     int best = T128x128;
     double best_cost = 1e300;
     for (int c = 0; c < kNumTiles; ++c) {
+        if (c == T64x128x2 && !two_per_cu) continue;
         const int bm = kTileBM[c], bn = kTileBN[c], bnc = (bn + frag_rows - 1) / frag_rows * frag_rows;
         const long tiles = long((M + bm - 1) / bm) * long((N + bn - 1) / bn);
-        const long waves = (tiles + 255) / 256;
-        const double eff = bm == 128 ? 1.0 : 0.9;
-        const double cost = double(waves) * bm * bnc / eff;
+        const int per_wave = c == T64x128x2 ? 512 : 256;
+        const long waves = (tiles + per_wave - 1) / per_wave;
+        const double eff = c == T64x128x2 ? (four_bit ? 1.15 : 0.95) : bm == 128 ? 1.0 : 0.9;
+        const double cost = double(waves) * (per_wave / 256) * bm * bnc / eff;
         if (cost < best_cost * 0.999) {
             best_cost = cost;
             best = c;
@@ -821,7 +865,9 @@ int tile_override() {
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream) {
     int tile = tile_override();
-    if (tile < 0) tile = choose_tile(g.M, g.N, g.abits == 8 && g.wbits == 8 && mfma_form() == 16 ? 16 : 32);
+    if (tile < 0)
+        tile = choose_tile(g.M, g.N, g.abits == 8 && g.wbits == 8 && mfma_form() == 16 ? 16 : 32,
+                           g.abits == 4 || g.wbits == 4, g.abits == g.wbits);
     if (g.abits == 8 && g.wbits == 8) return launch_tile<8, 8>(tile, g, stream);
     if (g.abits == 4 && g.wbits == 4) return launch_tile<4, 4>(tile, g, stream);
     if (g.abits == 8 && g.wbits == 4) return launch_tile<8, 4>(tile, g, stream);
