@@ -25,9 +25,13 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 
 // Two float32 -> bfloat16 conversions packed in one dword (lo in the low half),
 // round to nearest, ties to even: gfx950's v_cvt_pk_bf16_f32 (NaN -> quiet NaN).
+// (Written as one vector conversion: two scalar casts compile to two
+// conversions plus a shift and an or.)
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    const __bf16 a = static_cast<__bf16>(lo), b = static_cast<__bf16>(hi);
-    return uint32_t(__builtin_bit_cast(uint16_t, a)) | (uint32_t(__builtin_bit_cast(uint16_t, b)) << 16);
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t v = __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t);
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 // Operand fragments for v_mfma_i32_16x16x64_i8.  The MFMA sums over its 64 k
