@@ -670,39 +670,66 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, int tiles_m, int ti
         constexpr int XS = acc_stride<CF>();
         constexpr int shift = AccShift<ABITS, WBITS>::value;
         const int n = n_epi;
+        // output addresses: this lane's column n (head layout: its head's
+        // [M][head_dim] block) plus token row times the row stride, computed
+        // once and stepped by RPI rows per iteration
+        const int64_t ystride = g.head_dim > 0 ? g.head_dim : g.ldy;
+        int64_t ycol = n;
+        if (g.head_dim > 0) {
+            const int h = n / g.head_dim;
+            ycol = int64_t(h) * g.M * g.head_dim + (n - h * g.head_dim);
+        }
+        uint16_t* const yp0 = g.y + ycol + int64_t(m0 + rr[0]) * ystride;
+        int32_t* const ap0 = g.acc ? g.acc + n + int64_t(m0 + rr[0]) * g.N : nullptr;
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        // (one code path per bias/residual combination: as run-time
+        // conditions they became two selects per output)
+        auto run = [&](auto bias_tag, auto res_tag) {
+            constexpr bool kBias = decltype(bias_tag)::value;
+            constexpr bool kRes = decltype(res_tag)::value;
 #pragma unroll
-        for (int it = 0; it < NIT; ++it) {
-            if (!ok[it]) continue;
-            const int m = m0 + rr[it];
-            const v4i x0 = *reinterpret_cast<const v4i*>(X + rr[it] * XS + 8 * lc);
-            const v4i x1 = *reinterpret_cast<const v4i*>(X + rr[it] * XS + 8 * lc + 4);
-            const int a[8] = {x0[0] >> shift, x0[1] >> shift, x0[2] >> shift, x0[3] >> shift,
-                              x1[0] >> shift, x1[1] >> shift, x1[2] >> shift, x1[3] >> shift};
-            const float sw[8] = {sw0.x, sw0.y, sw0.z, sw0.w, sw1.x, sw1.y, sw1.z, sw1.w};
-            const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-            const uint32_t rw[4] = {rs[it].x, rs[it].y, rs[it].z, rs[it].w};
-            uint32_t o[4];
+            for (int it = 0; it < NIT; ++it) {
+                if (!ok[it]) continue;
+                const v4i x0 = *reinterpret_cast<const v4i*>(X + rr[it] * XS + 8 * lc);
+                const v4i x1 = *reinterpret_cast<const v4i*>(X + rr[it] * XS + 8 * lc + 4);
+                const int a[8] = {x0[0] >> shift, x0[1] >> shift, x0[2] >> shift, x0[3] >> shift,
+                                  x1[0] >> shift, x1[1] >> shift, x1[2] >> shift, x1[3] >> shift};
+                const float sw[8] = {sw0.x, sw0.y, sw0.z, sw0.w, sw1.x, sw1.y, sw1.z, sw1.w};
+                const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+                const uint32_t rw[4] = {rs[it].x, rs[it].y, rs[it].z, rs[it].w};
+                uint32_t o[4];
 #pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-                float t0 = float(a[e]) * (sa[it] * sw[e]);
-                float t1 = float(a[e + 1]) * (sa[it] * sw[e + 1]);
-                if (g.bias) {
-                    t0 = t0 + bb[e];
-                    t1 = t1 + bb[e + 1];
+                for (int e = 0; e < 8; e += 2) {
+                    float t0 = float(a[e]) * (sa[it] * sw[e]);
+                    float t1 = float(a[e + 1]) * (sa[it] * sw[e + 1]);
+                    if constexpr (kBias) {
+                        t0 = t0 + bb[e];
+                        t1 = t1 + bb[e + 1];
+                    }
+                    if constexpr (kRes) {
+                        t0 = t0 + bf16_lo(rw[e / 2]);
+                        t1 = t1 + bf16_hi(rw[e / 2]);
+                    }
+                    o[e / 2] = pack_bf16x2(t0, t1);
                 }
-                if (g.residual) {
-                    t0 = t0 + bf16_lo(rw[e / 2]);
-                    t1 = t1 + bf16_hi(rw[e / 2]);
+                *reinterpret_cast<uint4*>(yp0 + int64_t(it * RPI) * ystride) = make_uint4(o[0], o[1], o[2], o[3]);
+                if (ap0) {
+                    int32_t* ap = ap0 + int64_t(it * RPI) * g.N;
+                    *reinterpret_cast<int4*>(ap) = make_int4(a[0], a[1], a[2], a[3]);
+                    *reinterpret_cast<int4*>(ap + 4) = make_int4(a[4], a[5], a[6], a[7]);
                 }
-                o[e / 2] = pack_bf16x2(t0, t1);
             }
-            *reinterpret_cast<uint4*>(out_ptr(g, m, n)) = make_uint4(o[0], o[1], o[2], o[3]);
-            if (g.acc) {
-                int32_t* ap = g.acc + int64_t(m) * g.N + n;
-                *reinterpret_cast<int4*>(ap) = make_int4(a[0], a[1], a[2], a[3]);
-                *reinterpret_cast<int4*>(ap + 4) = make_int4(a[4], a[5], a[6], a[7]);
-            }
+        };
+        if (g.bias) {
+            if (g.residual)
+                run(std::true_type{}, std::true_type{});
+            else
+                run(std::true_type{}, std::false_type{});
+        } else {
+            if (g.residual)
+                run(std::false_type{}, std::true_type{});
+            else
+                run(std::false_type{}, std::false_type{});
         }
     }
 }
