@@ -27,6 +27,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <type_traits>
 
 #include "fq_device.h"
 #include "fq_internal.h"
@@ -281,7 +282,10 @@ __global__ __launch_bounds__(kMaxThreads) void prologue_kernel(const uint16_t* _
     // Codes.  |h| <= amax and s is amax / qmax rounded, so |h / s| stays below
     // qmax + 1/2 and round-half-even never leaves [-qmax, qmax]: the clamp of
     // the definition is implied and not executed.
-    if (active) {
+    // (one code path per divide form: as a per-element condition it cost a
+    // branch around every element's fallback divide)
+    auto quantise = [&](auto fast_tag) {
+        constexpr bool kFast = decltype(fast_tag)::value;
         constexpr int G = E < 16 ? E : 16;  // codes per store
 #pragma unroll
         for (int grp = 0; grp < E / G; ++grp) {
@@ -290,7 +294,7 @@ __global__ __launch_bounds__(kMaxThreads) void prologue_kernel(const uint16_t* _
             for (int i = 0; i < G; ++i) {
                 const float h = v[G * grp + i];
                 float qf;
-                if (fast) {
+                if constexpr (kFast) {
                     const float q0 = h * r;
                     const float rem = __builtin_fmaf(-s, q0, h);
                     qf = __builtin_fmaf(rem, r, q0);
@@ -329,6 +333,12 @@ __global__ __launch_bounds__(kMaxThreads) void prologue_kernel(const uint16_t* _
                     *reinterpret_cast<uint32_t*>(dst) = w[0];
             }
         }
+    };
+    if (active) {
+        if (fast)
+            quantise(std::true_type{});
+        else
+            quantise(std::false_type{});
     }
     if (c == 0) act_scale[m] = s;
 }
