@@ -20,6 +20,19 @@ __device__ __forceinline__ uint2 load_stream8(const uint8_t* p) {
     return make_uint2(v[0], v[1]);
 }
 
+// device-scope (sc1) stores: written through to memory as they are made
+__device__ __forceinline__ void store_dev16(void* p, uint4 v) {
+    const u32x4 d = {v.x, v.y, v.z, v.w};
+    asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(d) : "memory");
+}
+__device__ __forceinline__ void store_dev8(void* p, uint2 v) {
+    const u32x2 d = {v.x, v.y};
+    asm volatile("global_store_dwordx2 %0, %1, off sc1" ::"v"(p), "v"(d) : "memory");
+}
+__device__ __forceinline__ void store_dev4(void* p, uint32_t v) {
+    asm volatile("global_store_dword %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 

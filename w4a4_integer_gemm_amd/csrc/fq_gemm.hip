@@ -712,7 +712,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, int tiles_m, int ti
                     }
                     o[e / 2] = pack_bf16x2(t0, t1);
                 }
-                *reinterpret_cast<uint4*>(yp0 + int64_t(it * RPI) * ystride) = make_uint4(o[0], o[1], o[2], o[3]);
+                store_dev16(yp0 + int64_t(it * RPI) * ystride, make_uint4(o[0], o[1], o[2], o[3]));
                 if (ap0) {
                     int32_t* ap = ap0 + int64_t(it * RPI) * g.N;
                     *reinterpret_cast<int4*>(ap) = make_int4(a[0], a[1], a[2], a[3]);

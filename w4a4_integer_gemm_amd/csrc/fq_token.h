@@ -64,30 +64,80 @@ __device__ __forceinline__ double wave_sum(double v) {
     return v;
 }
 
-// value held by lane (lane ^ d) of the same wave, d in {1, 2, 4, 8}, via DPP
-template <int D>
-__device__ __forceinline__ float lane_xor(float v) {
-    const int i = __float_as_int(v);
-    if (D == 1) return __int_as_float(__builtin_amdgcn_mov_dpp(i, 0xB1, 0xF, 0xF, true));  // quad_perm [1,0,3,2]
-    if (D == 2) return __int_as_float(__builtin_amdgcn_mov_dpp(i, 0x4E, 0xF, 0xF, true));  // quad_perm [2,3,0,1]
-    if (D == 4) {
-        // xor 4 = (xor 7 within 8 lanes: row_half_mirror) then (xor 3: quad_perm [3,2,1,0])
-        const int m = __builtin_amdgcn_mov_dpp(i, 0x141, 0xF, 0xF, true);
-        return __int_as_float(__builtin_amdgcn_mov_dpp(m, 0x1B, 0xF, 0xF, true));
-    }
-    // xor 8 = (xor 15 within 16 lanes: row_mirror) then (xor 7: row_half_mirror)
-    const int m = __builtin_amdgcn_mov_dpp(i, 0x140, 0xF, 0xF, true);
-    return __int_as_float(__builtin_amdgcn_mov_dpp(m, 0x141, 0xF, 0xF, true));
-}
+// One cross-lane butterfly stage.  The lower lane of each pair keeps lo + hi;
+// the upper lane keeps lo - hi NEGATED, computed as own + (-1) * partner.  That
+// makes the partner's value the multiplied operand of one v_fmac_f32 that reads
+// it through DPP, one instruction per value where a DPP move and an fma took
+// two.  The negation is exact and round-to-nearest is symmetric, so each stored
+// value is the butterfly's value times a per-lane sign (the product of the
+// stages' signs), bit for bit; the caller removes it with the final 1/sqrt(b)
+// scaling.  Stages run with increasing distance, so a pair's two lanes always
+// carry the same sign from the earlier stages.
+//
+// The compiler does not fold a DPP move into v_fmac_f32, so the stage is
+// written out: blocks of 8 values, each opened with 5 wait states (a VALU
+// write of a VGPR or of EXEC before a DPP read) and closed with 2 (a DPP read
+// after the block).  Distances 4 and 8 take two lane permutations, the first
+// as a plain DPP move into a temporary.
+#define FQ_DPPM " row_mask:0xf bank_mask:0xf\n\t"
+#define FQ_FMAC8(C)                                                                                        \
+    "s_nop 4\n\t"                                                                                          \
+    "v_fmac_f32_dpp %0, %0, %8 " C FQ_DPPM "v_fmac_f32_dpp %1, %1, %8 " C FQ_DPPM                           \
+    "v_fmac_f32_dpp %2, %2, %8 " C FQ_DPPM "v_fmac_f32_dpp %3, %3, %8 " C FQ_DPPM                           \
+    "v_fmac_f32_dpp %4, %4, %8 " C FQ_DPPM "v_fmac_f32_dpp %5, %5, %8 " C FQ_DPPM                           \
+    "v_fmac_f32_dpp %6, %6, %8 " C FQ_DPPM "v_fmac_f32_dpp %7, %7, %8 " C FQ_DPPM "s_nop 1"
+#define FQ_MOVFMAC8(P, C)                                                                                  \
+    "s_nop 4\n\t"                                                                                          \
+    "v_mov_b32_dpp %8, %0 " P FQ_DPPM "v_mov_b32_dpp %9, %1 " P FQ_DPPM                                     \
+    "v_mov_b32_dpp %10, %2 " P FQ_DPPM "v_mov_b32_dpp %11, %3 " P FQ_DPPM                                   \
+    "v_mov_b32_dpp %12, %4 " P FQ_DPPM "v_mov_b32_dpp %13, %5 " P FQ_DPPM                                   \
+    "v_mov_b32_dpp %14, %6 " P FQ_DPPM "v_mov_b32_dpp %15, %7 " P FQ_DPPM "s_nop 1\n\t"                     \
+    "v_fmac_f32_dpp %0, %8, %16 " C FQ_DPPM "v_fmac_f32_dpp %1, %9, %16 " C FQ_DPPM                         \
+    "v_fmac_f32_dpp %2, %10, %16 " C FQ_DPPM "v_fmac_f32_dpp %3, %11, %16 " C FQ_DPPM                       \
+    "v_fmac_f32_dpp %4, %12, %16 " C FQ_DPPM "v_fmac_f32_dpp %5, %13, %16 " C FQ_DPPM                       \
+    "v_fmac_f32_dpp %6, %14, %16 " C FQ_DPPM "v_fmac_f32_dpp %7, %15, %16 " C FQ_DPPM "s_nop 1"
 
-// one cross-lane butterfly stage: the lower lane of each pair keeps lo + hi,
-// the upper lane lo - hi (sign * v is exact, so the fma rounds exactly once)
 template <int D, int E>
 __device__ __forceinline__ void cross_stage(float (&v)[E], int lane) {
+    static_assert(E % 8 == 0, "cross-lane stages work on blocks of 8 values");
     const float sgn = (lane & D) ? -1.0f : 1.0f;
 #pragma unroll
-    for (int i = 0; i < E; ++i) v[i] = __builtin_fmaf(sgn, v[i], lane_xor<D>(v[i]));
+    for (int b = 0; b < E / 8; ++b) {
+        float* const p = &v[8 * b];
+        if constexpr (D == 1 || D == 2) {
+            // D = 1: quad_perm [1,0,3,2]; D = 2: quad_perm [2,3,0,1]
+            if constexpr (D == 1)
+                asm volatile(FQ_FMAC8("quad_perm:[1,0,3,2]")
+                             : "+v"(p[0]), "+v"(p[1]), "+v"(p[2]), "+v"(p[3]), "+v"(p[4]), "+v"(p[5]), "+v"(p[6]),
+                               "+v"(p[7])
+                             : "v"(sgn));
+            else
+                asm volatile(FQ_FMAC8("quad_perm:[2,3,0,1]")
+                             : "+v"(p[0]), "+v"(p[1]), "+v"(p[2]), "+v"(p[3]), "+v"(p[4]), "+v"(p[5]), "+v"(p[6]),
+                               "+v"(p[7])
+                             : "v"(sgn));
+        } else {
+            // D = 4: row_half_mirror (xor 7 within 8 lanes), then quad_perm [3,2,1,0] (xor 3);
+            // D = 8: row_mirror (xor 15 within 16 lanes), then row_half_mirror (xor 7)
+            float t[8];
+            if constexpr (D == 4)
+                asm volatile(FQ_MOVFMAC8("row_half_mirror", "quad_perm:[3,2,1,0]")
+                             : "+v"(p[0]), "+v"(p[1]), "+v"(p[2]), "+v"(p[3]), "+v"(p[4]), "+v"(p[5]), "+v"(p[6]),
+                               "+v"(p[7]), "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(t[4]),
+                               "=&v"(t[5]), "=&v"(t[6]), "=&v"(t[7])
+                             : "v"(sgn));
+            else
+                asm volatile(FQ_MOVFMAC8("row_mirror", "row_half_mirror")
+                             : "+v"(p[0]), "+v"(p[1]), "+v"(p[2]), "+v"(p[3]), "+v"(p[4]), "+v"(p[5]), "+v"(p[6]),
+                               "+v"(p[7]), "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(t[4]),
+                               "=&v"(t[5]), "=&v"(t[6]), "=&v"(t[7])
+                             : "v"(sgn));
+        }
+    }
 }
+#undef FQ_MOVFMAC8
+#undef FQ_FMAC8
+#undef FQ_DPPM
 
 __device__ __forceinline__ void unpack8(uint4 d, float* o) {
     o[0] = bf16_lo(d.x);
@@ -245,8 +295,11 @@ __device__ __forceinline__ float quantise_loaded(const TokenLoad<E, NORM>& t, in
     if constexpr (hblock > 2 * E) cross_stage<2, E>(v, lane);
     if constexpr (hblock > 4 * E) cross_stage<4, E>(v, lane);
     if constexpr (hblock > 8 * E) cross_stage<8, E>(v, lane);
+    // the cross stages' sign: -1 for an odd number of set lane bits among those they used
+    constexpr int kCrossBits = hblock > E ? hblock / E - 1 : 0;
+    const float rs_lane = (__builtin_popcount(lane & kCrossBits) & 1) ? -rs : rs;
 #pragma unroll
-    for (int i = 0; i < E; ++i) v[i] = v[i] * rs;
+    for (int i = 0; i < E; ++i) v[i] = v[i] * rs_lane;
 
     if (AMODE == 2) divide_by_vector<E>(v, ascale, c, active);
 
