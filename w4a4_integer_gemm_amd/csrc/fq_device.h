@@ -20,7 +20,10 @@ __device__ __forceinline__ uint2 load_stream8(const uint8_t* p) {
     return make_uint2(v[0], v[1]);
 }
 
-// device-scope (sc1) stores: written through to memory as they are made
+// Device-scope (sc1) stores: written through L2 as they are made, so that a
+// kernel's output is not left dirty in L2 for the write-back at its end.  The
+// compiler does not count these stores in its memory-counter waits; they only
+// add to the count, so its waits for its own loads stay long enough.
 __device__ __forceinline__ void store_dev16(void* p, uint4 v) {
     const u32x4 d = {v.x, v.y, v.z, v.w};
     asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(d) : "memory");

@@ -322,7 +322,8 @@ __device__ __forceinline__ float quantise_loaded(const TokenLoad<E, NORM>& t, in
     // branch around every element's fallback divide)
     auto quantise = [&](auto fast_tag) {
         constexpr bool kFast = decltype(fast_tag)::value;
-        constexpr int G = E < 16 ? E : 16;  // codes per store
+        // codes per store: at most 16 bytes of them
+        constexpr int G = ABITS == 8 ? (E < 16 ? E : 16) : (E < 32 ? E : 32);
 #pragma unroll
         for (int grp = 0; grp < E / G; ++grp) {
             uint32_t t[G];
@@ -361,7 +362,9 @@ __device__ __forceinline__ float quantise_loaded(const TokenLoad<E, NORM>& t, in
                     for (int j = 0; j < 8; ++j) acc |= (t[8 * i + j] & 0xFu) << (4 * j);
                     w[i] = acc;
                 }
-                if constexpr (G == 16)
+                if constexpr (G == 32)
+                    store((E / 2) * c + (G / 2) * grp, make_uint4(w[0], w[1], w[2], w[3]));
+                else if constexpr (G == 16)
                     store((E / 2) * c + (G / 2) * grp, make_uint2(w[0], w[1]));
                 else
                     store((E / 2) * c + (G / 2) * grp, w[0]);
