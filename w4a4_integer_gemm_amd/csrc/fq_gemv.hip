@@ -306,19 +306,34 @@ __global__ __launch_bounds__(64 * kStreamWaves) __attribute__((amdgpu_waves_per_
     const int last = J - 1;
     if (loader && J > 0) issue(wa, 0);
 
-    // the tokens' codes and scales into LDS; rows M .. 16 MT - 1 are zero
+    // the tokens' codes and scales into LDS; rows M .. 16 MT - 1 are zero.
+    // A thread's pieces are requested kBatch at a time before any is written,
+    // so the copy waits for one load latency per batch, not one per piece.
     {
+        const float sc = tid < g.M ? g.act_scale[tid] : 0.0f;
         const int kb = g.K * ABITS / 8;
         const int pieces = kb >> 4;
         const int total = 16 * MT * pieces;
-        for (int i = tid; i < total; i += 64 * kStreamWaves) {
-            const int r = i / pieces;
-            const int cc = i - r * pieces;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (r < g.M) v = *reinterpret_cast<const uint4*>(g.act + int64_t(r) * kb + cc * 16);
-            *reinterpret_cast<uint4*>(act_lds + r * pitch + cc * 16) = v;
+        constexpr int kBatch = 8;
+        constexpr int kStride = 64 * kStreamWaves;
+        for (int i0 = tid; i0 < total; i0 += kBatch * kStride) {
+            uint4 v[kBatch];
+#pragma unroll
+            for (int b = 0; b < kBatch; ++b) {
+                const int i = i0 + b * kStride;
+                const int r = i / pieces;
+                v[b] = make_uint4(0, 0, 0, 0);
+                if (i < total && r < g.M)
+                    v[b] = *reinterpret_cast<const uint4*>(g.act + int64_t(r) * kb + (i - r * pieces) * 16);
+            }
+#pragma unroll
+            for (int b = 0; b < kBatch; ++b) {
+                const int i = i0 + b * kStride;
+                const int r = i / pieces;
+                if (i < total) *reinterpret_cast<uint4*>(act_lds + r * pitch + (i - r * pieces) * 16) = v[b];
+            }
         }
-        if (tid < g.M) scale_lds[tid] = g.act_scale[tid];
+        if (tid < g.M) scale_lds[tid] = sc;
     }
     __syncthreads();
 
