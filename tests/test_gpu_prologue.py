@@ -14,10 +14,13 @@ from fqtest import assert_codes, dev, host, log
 pytestmark = pytest.mark.gpu
 
 CASES = [
-    # M, K, hblock, abits, norm, ascale mode, fold_after.  Values per lane: 16 for
-    # K <= 8192 (a 256-block then spans 16 lanes: the xor-8 exchange), 32 up to
-    # K = 32768, 64 beyond
+    # M, K, hblock, abits, norm, ascale mode, fold_after.  Values per lane: 8 for
+    # M <= 32, K <= 2048 and hblock <= 128 (a 128-block spans 16 lanes), else 16
+    # for K <= 8192 (a 256-block then spans 16 lanes: the xor-8 exchange), 32 up
+    # to K = 32768, 64 beyond
     (1, 64, 1, 8, False, "none", 0),
+    (4, 2016, 8, 8, True, "gain", 0),       # 8 values per lane, 252 lanes (last wave ragged)
+    (32, 1024, 128, 8, True, "explicit", 1),  # the last token count with 8 values per lane
     (3, 64, 64, 4, True, "gain", 0),
     (16, 256, 64, 8, True, "gain", 0),
     (7, 256, 2, 8, True, "explicit", 0),

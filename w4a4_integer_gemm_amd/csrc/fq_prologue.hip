@@ -3,14 +3,17 @@
 // RMSNorm with the folded gain, the ascale divide, the block rotation, a
 // per-token amax scale, round-half-even and a clamp).
 //
-// Layout: one workgroup per token.  Lane t owns E = 16 (K <= 8192), 32
-// (K <= 32768) or 64 consecutive bf16 values (E/8 16-byte loads), so a token
-// of up to 65536 values is one pass of at most 1024 lanes.  The butterfly's
+// Layout: one workgroup per token.  Lane t owns E = 8 (at most 32 tokens of
+// at most 2048 values), 16 (K <= 8192), 32 (K <= 32768) or 64 consecutive
+// bf16 values (E/8 16-byte loads), so a token of up to 65536 values is one
+// pass of at most 1024 lanes.  The butterfly's
 // first log2(E) stages (span 1 .. E/2) run inside a lane's registers; a
 // Hadamard block of b > E values spans b/E (at most 16) consecutive lanes,
 // whose stages (span E .. b/2) exchange values with DPP lane permutations
-// (xor 1, xor 2, and xor 4 and xor 8 composed from two permutations) and one
-// fused multiply-add per value.  Every element goes
+// (xor 1, xor 2, and xor 4 and xor 8 composed from two permutations), one
+// multiply-add per value that reads the partner through DPP; the upper lane
+// of each pair keeps its result negated, and the final 1/sqrt(b) scaling
+// removes that sign (exact, so the values are unchanged bit for bit).  Every element goes
 // through the same float32 operations in the same order as the definition
 // (stage spans 1, 2, 4, ...), so the rotation is bit-reproducible.  The token
 // stays in registers between the two reductions (sum of squares, amax): x is
@@ -37,6 +40,13 @@ namespace fq {
 namespace {
 
 constexpr int kMaxThreads = 1024;
+// Few tokens of at most 2048 values take 8 values per lane: no two
+// workgroups then share a SIMD's issue, and the shorter per-lane chain wins
+// while the cross-wave reductions stay within 4 waves (graph-replayed, one
+// launch: 16 x 256 2.84 -> 2.59 us, 16 x 2048 3.30 -> 3.19 us; at K = 3584,
+// 7 waves, 3.24 -> 3.39 us, so 16 values there).
+constexpr int kFewTokens = 32;
+constexpr int kFewTokensMaxK = 2048;
 constexpr int kMaxWaves = kMaxThreads / 64;
 
 // One workgroup per token; lane t owns values [E t, E t + E) of the token.
@@ -82,9 +92,13 @@ __global__ __launch_bounds__(kMaxThreads) void prologue_kernel(const uint16_t* _
 
 template <int E, int ABITS, bool NORM, int AMODE, int LOG2B>
 hipError_t launch_e(dim3 grid, dim3 block, hipStream_t st, const PrologueArgs& a, float rs) {
-    hipLaunchKernelGGL((prologue_kernel<E, ABITS, NORM, AMODE, LOG2B>), grid, block, 0, st, a.x, a.K, a.ldx, a.gamma,
-                       a.eps, a.ascale, rs, a.codes, a.act_scale);
-    return hipGetLastError();
+    if constexpr ((1 << LOG2B) > 16 * E) {
+        return hipErrorInvalidValue;  // not chosen by launch_prologue
+    } else {
+        hipLaunchKernelGGL((prologue_kernel<E, ABITS, NORM, AMODE, LOG2B>), grid, block, 0, st, a.x, a.K, a.ldx,
+                           a.gamma, a.eps, a.ascale, rs, a.codes, a.act_scale);
+        return hipGetLastError();
+    }
 }
 
 template <int E, int ABITS, bool NORM, int AMODE>
@@ -120,18 +134,25 @@ hipError_t launch_modes(dim3 grid, dim3 block, hipStream_t st, const PrologueArg
 
 }  // namespace
 
-// Values per lane: 16 up to K = 8192: each token is a chain of dependent
+// Values per lane: 8 for a few short tokens (above), else 16 up to K = 8192:
+// each token is a chain of dependent
 // steps, and halving a lane's share shortens it (measured on the qkv prologue,
 // K = 3584: 7.0 -> 6.0 us for 1024 tokens, 4.0 -> 3.4 us for one; 8 per lane
 // gained nothing more); 32 up to K = 32768 (one pass of at most 1024 lanes),
 // 64 beyond.
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t stream) {
-    const int E = a.K <= 8192 ? 16 : a.K > 32768 ? 64 : 32;
+    // (a Hadamard block spans at most 16 lanes: 8 values per lane only for b <= 128)
+    const int E = a.M <= kFewTokens && a.K <= kFewTokensMaxK && a.hblock <= 128 ? 8
+                  : a.K <= 8192                                         ? 16
+                  : a.K > 32768                                         ? 64
+                                                                        : 32;
     const int nlanes = a.K / E;
     const int T = (nlanes + 63) / 64 * 64;
     if (T > kMaxThreads) return hipErrorInvalidValue;
     const float rs = float(1.0 / std::sqrt(double(a.hblock)));
     dim3 grid(a.M), block(T);
+    if (E == 8)
+        return a.abits == 8 ? launch_modes<8, 8>(grid, block, stream, a, rs) : launch_modes<8, 4>(grid, block, stream, a, rs);
     if (E == 16)
         return a.abits == 8 ? launch_modes<16, 8>(grid, block, stream, a, rs) : launch_modes<16, 4>(grid, block, stream, a, rs);
     if (E == 32)

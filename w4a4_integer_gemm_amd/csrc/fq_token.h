@@ -240,6 +240,7 @@ __device__ __forceinline__ float quantise_loaded(const TokenLoad<E, NORM>& t, in
                                                  float eps, const float* __restrict__ ascale, float rs, int c,
                                                  int nwaves, double* red_d, float* red_f, Store store) {
     constexpr int hblock = 1 << LOG2B;
+    static_assert(hblock <= 16 * E, "a Hadamard block spans at most 16 lanes (cross-lane distances 1 .. 8)");
     constexpr int qmax = ABITS == 8 ? 127 : 7;
     const int lane = c & 63;
     const int wave = c >> 6;
