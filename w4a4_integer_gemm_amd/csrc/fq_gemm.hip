@@ -356,11 +356,14 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, int tiles_m, int ti
                 copy16_to_lds(base, off, lds0 + uint32_t(slot * CF::STAGE + ldsoff[i]));
             }
         };
-        // stages 0 .. NS-2 (clamped to the last stage when K is short), then
-        // publish stage 0
-        for (int s = 0; s < CF::NS - 1; ++s) load_stage(s < nk ? s : nk - 1, s);
-        wait_vmcnt<(CF::NS - 2) * CF::NHI>();
+        // stage 0 alone, published as soon as it lands, then stages 1 .. NS-2
+        // (clamped to the last stage when K is short): at launch every CU's
+        // first stage then queues ahead of the others' prefetch (qkv 19.50 ->
+        // 19.30 us, down 64.09 -> 63.64 us against issuing all NS - 1 first)
+        load_stage(0, 0);
+        wait_vmcnt<0>();
         barrier_nofence();
+        for (int s = 1; s < CF::NS - 1; ++s) load_stage(s < nk ? s : nk - 1, s);
         // After barrier s-1 every MFMA wave is done with stage s-1, whose slot
         // takes stage s + NS - 1 while that is a stage of K.  Barrier s
         // publishes stage s + 1: the wait lets the stages issued after it stay
