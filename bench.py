@@ -38,23 +38,34 @@ def site_for(wl):
                          fold_after=wl.fold_after, fold_into_gain=wl.fold_into_gain, bias=wl.bias, eps=wl.eps)
 
 
-def time_loop(fn, iters):
-    """Average ms per call of fn() over iters back-to-back calls, HIP events on the current stream."""
+WARM_MS = 25.0  # untimed work before a timed region: the clock needs 5-10 ms of load to settle
+
+
+def warm_up(step, warmup, min_ms=WARM_MS):
+    """At least `warmup` calls, and then more in groups of 20 until min_ms of
+    wall time has passed (host-synchronized), so that a timed region starts at
+    the clock the part holds under steady load.  Returns the calls run."""
     import torch
-    s = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(s)
-    for _ in range(iters):
-        fn()
-    e1.record(s)
-    e1.synchronize()
-    return e0.elapsed_time(e1) / iters
+    n = 0
+    t0 = time.perf_counter()
+    for _ in range(warmup):
+        step()
+        n += 1
+    torch.cuda.synchronize()
+    while (time.perf_counter() - t0) * 1e3 < min_ms:
+        for _ in range(20):
+            step()
+        n += 20
+        torch.cuda.synchronize()
+    return n
 
 
 def timed_steps(step, steps, batch=20):
-    """Time `steps` back-to-back calls between two synchronizations (the value
-    reported); HIP events recorded every `batch` calls inside the same region
-    give the spread: median, p10 and p90 of the batch means (ms per call)."""
+    """Time `steps` back-to-back calls launched from Python between two
+    synchronizations (the value reported; the graph-replayed figure goes next
+    to it);
+    HIP events recorded every `batch` calls inside the same region give the
+    spread: median, p10 and p90 of the batch means (ms per call)."""
     import torch
     s = torch.cuda.current_stream()
     marks = []
@@ -78,6 +89,52 @@ def timed_steps(step, steps, batch=20):
     return ms, stats
 
 
+def graph_steps(step, steps, batch=20):
+    """Time `steps` calls of step() replayed from HIP graphs: one graph holds
+    `batch` calls (replayed steps // batch times), another the remainder.
+    The timed region runs between two synchronizations; HIP events recorded
+    between replays give the spread: median, p10 and p90 of the batch means.
+    Returns (ms per call over the whole region, spread)."""
+    import torch
+    full, rem = divmod(steps, batch)
+
+    def capture(n):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(n):
+                step()
+        return g
+
+    gb = capture(batch) if full else None
+    gr = capture(rem) if rem else None
+    for g in (gb, gr):  # untimed first replays
+        if g is not None:
+            g.replay()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    marks = []
+    t0 = time.perf_counter()
+    for _ in range(full):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(s)
+        marks.append(e)
+        gb.replay()
+    e = torch.cuda.Event(enable_timing=True)
+    e.record(s)
+    marks.append(e)
+    if gr is not None:
+        gr.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    means = [a.elapsed_time(b) / batch for a, b in zip(marks, marks[1:])]
+    stats = None
+    if means:
+        stats = {"batch": batch, "batches": len(means), "median_ms": float(np.median(means)),
+                 "p10_ms": float(np.percentile(means, 10)), "p90_ms": float(np.percentile(means, 90))}
+    del gb, gr
+    return ms, stats
+
+
 def bench_prefill(name, steps, warmup):
     import torch
     import synth
@@ -88,19 +145,20 @@ def bench_prefill(name, steps, warmup):
     y = site.empty_out(wl.M)
     site.workspace(wl.M)
     step = lambda: site.linear(x, residual=res, y=y)
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    nwarm = warm_up(step, warmup)
     ms, batches = timed_steps(step, steps)
+    ms_graph, _ = graph_steps(step, steps)
     ops = 2.0 * wl.M * wl.N * wl.K
     codes, scales = site.workspace_codes(wl.M)
-    # per-kernel averages (HIP events around back-to-back launches of one kernel)
-    ms_pro = time_loop(lambda: site.prologue(x, codes, scales), steps)
-    ms_gemm = time_loop(lambda: site.gemm(codes, scales, wl.M, residual=res, y=y), steps)
+    # per-kernel averages (HIP events around graph replays of back-to-back launches of one kernel)
+    ms_pro, _ = graph_steps(lambda: site.prologue(x, codes, scales), steps)
+    ms_gemm, _ = graph_steps(lambda: site.gemm(codes, scales, wl.M, residual=res, y=y), steps)
     site.linear(x, residual=res, y=y)
     torch.cuda.synchronize()
     ok, detail = parity(wl, site, y, codes, scales)
-    return dict(wl=wl, ms=ms, tops=ops / (ms * 1e-3) / 1e12, ms_prologue=ms_pro, ms_gemm=ms_gemm,
+    return dict(wl=wl, ms=ms, tops=ops / (ms * 1e-3) / 1e12, ms_prologue=ms_pro, ms_gemm=ms_gemm, ms_graph=ms_graph,
+                warmup_run=nwarm,
+                tops_graph=ops / (ms_graph * 1e-3) / 1e12,
                 gemm_tops=ops / (ms_gemm * 1e-3) / 1e12, parity=detail, parity_ok=ok, ops=ops, batches=batches)
 
 
@@ -146,10 +204,9 @@ def bench_decode(name, steps, warmup, copies=5):
         sites[k].linear(x, y=ys[k])
         i[0] += 1
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    nwarm = warm_up(step, warmup)
     ms, batches = timed_steps(step, steps)
+    ms_graph, _ = graph_steps(step, steps)
     wbytes = wl.N * wl.K * wl.wbits / 8
     # algorithmic bytes: weight codes + weight scales + x + y + activation codes written and read back
     nbytes = wbytes + 4 * wl.N + 2 * wl.M * wl.K + 2 * wl.M * wl.N + 2 * wl.M * wl.K * wl.abits / 8 + 8 * wl.M
@@ -163,9 +220,11 @@ def bench_decode(name, steps, warmup, copies=5):
         sites[k].gemm(c, sc, wl.M, y=ys[k])
         j[0] += 1
 
-    ms_gemv = time_loop(gemv, steps)
+    ms_gemv, _ = graph_steps(gemv, steps)
     gemv_bytes = wbytes + 4 * wl.N + wl.M * wl.K * wl.abits / 8 + 4 * wl.M + 2 * wl.M * wl.N
-    return dict(name=name, M=wl.M, ms=ms, gbs=nbytes / (ms * 1e-3) / 1e9, ms_gemv=ms_gemv,
+    return dict(name=name, M=wl.M, ms=ms, gbs=nbytes / (ms * 1e-3) / 1e9, ms_gemv=ms_gemv, ms_graph=ms_graph,
+                warmup_run=nwarm,
+                gbs_graph=nbytes / (ms_graph * 1e-3) / 1e9,
                 gemv_gbs=gemv_bytes / (ms_gemv * 1e-3) / 1e9, bytes=nbytes, gemv_bytes=gemv_bytes, batches=batches)
 
 
@@ -301,6 +360,7 @@ def main():
             s = bench_prefill(name, max(20, args.steps // 4), args.warmup)
             secondary.append({"workload": name, "metric": "fq_linear TOPS", "value": s["tops"],
                               "frac_int8_peak": s["tops"] / PEAK_INT8_TOPS, "ms_per_call": s["ms"],
+                              "graph": {"value": s["tops_graph"], "ms_per_call": s["ms_graph"]},
                               "batch_spread": s["batches"], "gemm_tops": s["gemm_tops"],
                               "ms_prologue": s["ms_prologue"], "ms_gemm": s["ms_gemm"], "parity": s["parity"]})
             del s
@@ -308,12 +368,14 @@ def main():
         # the tiny 16-token site: latency only
         s = bench_prefill("tiny_w8a8", max(50, args.steps), args.warmup)
         secondary.append({"workload": "tiny_w8a8", "metric": "fq_linear latency", "value": s["ms"] * 1e3,
-                          "unit": "us", "batch_spread": s["batches"], "parity": s["parity"]})
+                          "unit": "us", "batch_spread": s["batches"], "graph": {"value": s["ms_graph"] * 1e3},
+                          "parity": s["parity"]})
         del s
         for name in ("decode_m1_w8a8", "decode_m16_w8a8"):
             d = bench_decode(name, max(50, args.steps), args.warmup)
             secondary.append({"workload": name, "metric": "decode GB/s", "value": d["gbs"],
                               "frac_hbm": d["gbs"] / PEAK_HBM_GBS, "ms_per_call": d["ms"],
+                              "graph": {"value": d["gbs_graph"], "ms_per_call": d["ms_graph"]},
                               "batch_spread": d["batches"],
                               "gemv_gbs": d["gemv_gbs"], "gemv_frac_hbm": d["gemv_gbs"] / PEAK_HBM_GBS,
                               "ms_gemv": d["ms_gemv"], "algorithmic_bytes": d["bytes"],
@@ -338,6 +400,12 @@ def main():
                                f"W{wl.wbits}A{wl.abits} hblock={wl.hblock}, weights warm in HBM",
                    "global_batch": wl.M, "parallelism": "single GPU"},
         "frac_int8_peak": r["tops"] / PEAK_INT8_TOPS,
+        "timing": "value: the calls launched back to back from Python; 'graph': the same calls replayed from HIP "
+                  "graphs of 20 (no launch gaps; the large kernels then run slower); ms_prologue, ms_gemm "
+                  "and the roofline: one kernel replayed from graphs",
+        "graph": {"value": r["tops_graph"], "ms_per_step": r["ms_graph"]},
+        "warmup_steps_run": r["warmup_run"],
+        "warmup_rule": f"at least --warmup steps and at least {WARM_MS:g} ms of them before each timed region",
         "batch_spread": r["batches"],
         "ms_prologue": r["ms_prologue"],
         "ms_gemm": r["ms_gemm"],

@@ -1,0 +1,78 @@
+"""fq_linear captured in a HIP graph (as the benchmark replays it) gives the
+eager result on every replay: several replays, with eager work (new inputs
+written into the captured buffers, an eager fq_linear, host
+synchronizations) between them, each compared bit for bit with an eager
+call on the same inputs.  Covers the MFMA GEMM with a residual, the W4A4
+GEMM, the streaming decode GEMV (M = 16, weights rotated over two sites as
+in the benchmark) and the split-K GEMV (M = 1)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+import w4a4_integer_gemm_amd as fq
+from fqtest import dev, log
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # workload, M, N (shrunk where the full size adds nothing), copies
+    ("qkv_w8a8", 96, 1152, 1),
+    ("down_w8a8", 64, 512, 1),
+    ("gateup_w4a4", 80, 1024, 1),
+    ("decode_m16_w8a8", 16, 4096, 2),
+    ("decode_m1_w8a8", 1, 4096, 2),
+]
+
+
+def site_for(wl, codes=None, wscale=None):
+    return fq.DeviceSite(None if codes is not None else wl.W, wl.hblock, wl.wbits, wl.abits, gamma=wl.gamma,
+                         ascale=wl.ascale, fold_after=wl.fold_after, fold_into_gain=wl.fold_into_gain,
+                         bias=wl.bias, eps=wl.eps, codes=codes, wscale=wscale)
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c[0]}_M{c[1]}_N{c[2]}")
+def test_graph_replays_match_eager(case):
+    name, M, N, copies = case
+    log(f"graph case {case}")
+    wl = synth.make_workload(name, M=M, N=N)
+    base = site_for(wl)
+    sites = [base] + [site_for(wl, base.codes_host, base.wscale_host) for _ in range(copies - 1)]
+    x = dev(wl.x)
+    res = dev(wl.residual) if wl.residual is not None else None
+    ys = [s.empty_out(M) for s in sites]
+    for s in sites:
+        s.workspace(M)
+
+    def step_all():
+        for s, y in zip(sites, ys):
+            s.linear(x, residual=res, y=y)
+
+    step_all()  # first calls outside the capture (one-time device queries)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step_all()
+    rng = np.random.default_rng(7)
+    for rep in range(4):
+        # eager work between replays: fresh inputs into the captured buffers, and
+        # an eager call on them whose results the replay must reproduce
+        xn = wl.x if rep == 0 else wl.x[rng.permutation(M)]
+        if rep % 2:
+            xn = xn[:, ::-1]  # the same values in another order along K
+        x.copy_(dev(xn))
+        step_all()
+        torch.cuda.synchronize()
+        want = [y.clone() for y in ys]
+        want_codes = [torch.cat([c.view(torch.uint8).flatten() for c in s.workspace_codes(M)]).clone()
+                      for s in sites]
+        for y in ys:
+            y.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (s, y) in enumerate(zip(sites, ys)):
+            got_codes = torch.cat([c.view(torch.uint8).flatten() for c in s.workspace_codes(M)])
+            assert torch.equal(got_codes, want_codes[i]), f"{name} replay {rep} site {i}: codes differ from eager"
+            assert torch.equal(y, want[i]), f"{name} replay {rep} site {i}: y differs from eager"
+    del g
