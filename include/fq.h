@@ -31,14 +31,25 @@
  *   - Status codes: FQ_OK on success.  On any failure the call returns a code,
  *     sets a thread-local message (fq_last_error) that names the call, the
  *     argument and the arithmetic, writes nothing and queues no device work.
- *     No C++ exception crosses this ABI; nothing aborts.
+ *     The one exception is a launch refused by the HIP runtime after an
+ *     earlier launch of the same call was queued (fq_linear's GEMM after its
+ *     prologue): FQ_ERR_DEVICE then reports it, and the workspace may hold
+ *     the prologue's codes.  Every host-side step that can fail runs before
+ *     the first launch.  No C++ exception crosses this ABI; nothing aborts.
  *   - Ownership: the caller allocates and frees every buffer.  The library
- *     allocates no device memory, never synchronises, and keeps no state other
- *     than the error message.  Inputs are read only; outputs are overwritten.
+ *     allocates no device memory and never synchronises.  Inputs are read
+ *     only; outputs are overwritten.
+ *   - State kept by the library: the thread-local error message; per device,
+ *     a record made once per process on the first device call there (or by
+ *     fq_device_init): the compute-unit and LDS sizes, and the streaming
+ *     GEMV kernels' register-limited residency after raising their
+ *     dynamic-LDS limit; and the process-wide test hooks (fq_test_hook).
+ *     No call depends on an earlier call's data.
  *   - Device entry points are asynchronous on `stream` (a hipStream_t passed as
  *     void*; NULL is the null stream) and take device pointers.
  *   - Shapes: M, N >= 1; N a multiple of 8; K <= 65536, a multiple of 32 for
- *     fq_prologue and of 128 for fq_pack_weights, fq_gemm and fq_linear;
+ *     fq_prologue (of 64 when K > 32768) and of 128 for fq_pack_weights,
+ *     fq_dequant_rows, fq_gemm and fq_linear;
  *     hblock a power of two in [1, 256] dividing K (1 = no rotation); bits in
  *     {4, 8} for both weights and activations (W8A8, W4A4, W4A8, W8A4).
  *   - Alignment: bf16 rows (x, residual, y) need a 16-byte aligned base and a
@@ -74,6 +85,25 @@ const char* fq_last_error(void);
 
 /* FQ_ABI_VERSION of the built library. */
 int fq_abi_version(void);
+
+/* Optional set-up of the current HIP device: the per-device record described
+ * under "State kept by the library" above.  Every device entry point makes it
+ * itself on its first call on a device; calling this first keeps those HIP
+ * queries (attribute, occupancy) out of a graph capture that would otherwise
+ * contain the first call.  Idempotent; FQ_ERR_DEVICE if a query fails. */
+fq_status fq_device_init(void);
+
+/* Test hook, for the tests only: forces kernel choices that the shape would
+ * not get, so that every kernel variant can be checked against the oracle.
+ * spec: comma-separated key=value items, each call replacing the whole hook
+ * state; "" or NULL restores the defaults.
+ *   gemm_tile=<128x128|128x144|128x112|128x96|64x128|64x224|64x256|64x288|64x128x2|auto>
+ *   gemm_mfma=<16|32>     (8-bit x 8-bit codes on v_mfma_i32_32x32x32_i8 with 32)
+ *   gemv=<split|auto>     (decode-sized M always on the split-K GEMV kernel)
+ * The environment variable FQ_TEST_HOOK, read once per process at the hooks'
+ * first use, takes the same spec.  FQ_ERR_ARG on an unknown key or value (state kept).
+ * Process-wide; a call while another thread launches races with it. */
+fq_status fq_test_hook(const char* spec);
 
 /* ------------------------------------------------------------------ host, synchronous */
 

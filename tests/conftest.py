@@ -17,3 +17,12 @@ def pytest_configure(config):
 def oracle_lib():
     import oracle
     return oracle.lib()
+
+
+@pytest.fixture
+def hook():
+    """Sets libfq's test hook (fq_test_hook) for one test and restores the defaults after it."""
+    import w4a4_integer_gemm_amd as fq
+    fq.fq_test_hook("")
+    yield fq.fq_test_hook
+    fq.fq_test_hook("")

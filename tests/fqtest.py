@@ -38,6 +38,18 @@ def host(t, dtype=None):
     return a
 
 
+def rand_codes(rng, rows, K, bits, extreme=False):
+    """Random codes in [-qmax, qmax] (or all +-qmax), stored as the kernels read them."""
+    qmax = oracle.qmax(bits)
+    if extreme:
+        q = rng.choice([-qmax, qmax], size=(rows, K))
+    else:
+        q = rng.integers(-qmax, qmax + 1, size=(rows, K))
+    if bits == 8:
+        return q.astype(np.int8).view(np.uint8)
+    return ((q[:, 0::2] & 0xF) | ((q[:, 1::2] & 0xF) << 4)).astype(np.uint8)
+
+
 def bf16_to_f64(bits):
     return synth.bf16_bits_to_f32(np.ascontiguousarray(bits).view(np.uint16)).astype(np.float64)
 
@@ -67,22 +79,33 @@ def bf16_half_ulp(v):
     return 2.0 ** (e - 8)
 
 
-def assert_y_elementwise(y_gpu_bits, y_f64, acc, sa, sw, bias=None, residual_bits=None, what=""):
-    """Identical codes: each bf16 output within half a bf16 ulp of the oracle's
-    float64 value plus the float32 rounding of the epilogue."""
-    yg = bf16_to_f64(y_gpu_bits)
-    prod = np.abs(acc.astype(np.float64) * sa.astype(np.float64)[:, None] * sw.astype(np.float64)[None, :])
-    mag = prod.copy()
+def epilogue_magnitude(acc, sa, sw, bias=None, residual_bits=None):
+    """|acc * s_m * s_n| + |bias_n| + |residual_mn| per output: the scale of the
+    epilogue's float32 rounding."""
+    mag = np.abs(acc.astype(np.float64) * sa.astype(np.float64)[:, None] * sw.astype(np.float64)[None, :])
     if bias is not None:
-        mag += np.abs(bias.astype(np.float64))[None, :]
+        mag = mag + np.abs(bias.astype(np.float64))[None, :]
     if residual_bits is not None:
-        mag += np.abs(bf16_to_f64(residual_bits))
+        mag = mag + np.abs(bf16_to_f64(residual_bits))
+    return mag
+
+
+def assert_y_within(y_gpu_bits, y_f64, mag, what=""):
+    """Each bf16 output within half a bf16 ulp of the oracle's float64 value plus
+    the float32 rounding of the epilogue's three operations (2^-21 of `mag`)."""
+    yg = bf16_to_f64(y_gpu_bits)
     bound = bf16_half_ulp(y_f64) * (1 + 1e-6) + mag * 2.0 ** -21
     err = np.abs(yg - y_f64)
     bad = err > bound
     log(f"  {what} y: max err/bound {np.max(err / np.maximum(bound, 1e-300)):.3f}")
     assert not np.any(bad), f"{what}: {np.count_nonzero(bad)} outputs outside the bound, e.g. " \
                             f"{yg[bad][:4]} vs {y_f64[bad][:4]}"
+
+
+def assert_y_elementwise(y_gpu_bits, y_f64, acc, sa, sw, bias=None, residual_bits=None, what=""):
+    """Identical codes: each bf16 output within half a bf16 ulp of the oracle's
+    float64 value plus the float32 rounding of the epilogue."""
+    assert_y_within(y_gpu_bits, y_f64, epilogue_magnitude(acc, sa, sw, bias, residual_bits), what)
 
 
 def rel_fro(y_gpu_bits, y_f64):

@@ -292,3 +292,18 @@ def test_binding_refuses_host_tensors_for_device_calls():
     with pytest.raises(ValueError, match="GPU tensors"):
         fq.fq_prologue(torch.zeros(4, 64, dtype=torch.int16), 4, 64, 64, None, 1e-6, None, 0, 64, 8,
                        torch.zeros(256, dtype=torch.uint8), torch.zeros(4), None)
+
+
+def test_test_hook_parses_and_rejects():
+    """fq_test_hook takes "key=value" items and rejects unknown keys or values
+    with a message (host only: it touches no device)."""
+    L = _binding.lib()
+    for good in ("", "default", "gemm_tile=64x128x2", "gemm_tile=auto,gemm_mfma=32", "gemv=split",
+                 "gemm_tile=128x144,gemm_mfma=16,gemv=auto"):
+        assert L.fq_test_hook(good.encode()) == 0, good
+    assert L.fq_test_hook(None) == 0
+    for bad, what in (("gemm_tile=100x100", "unknown gemm_tile"), ("gemm_mfma=8", "gemm_mfma must be"),
+                      ("gemv=fast", "gemv must be"), ("tile=64x128", "unknown hook")):
+        assert L.fq_test_hook(bad.encode()) == 1, bad
+        assert what in _binding.last_error(), _binding.last_error()
+    assert L.fq_test_hook(b"") == 0

@@ -7,20 +7,9 @@ import numpy as np
 import pytest
 
 import oracle
-from fqtest import assert_y_elementwise, dev, host, log
+from fqtest import assert_y_elementwise, dev, host, log, rand_codes
 
 pytestmark = pytest.mark.gpu
-
-
-def rand_codes(rng, rows, K, bits, extreme=False):
-    qmax = oracle.qmax(bits)
-    if extreme:
-        q = rng.choice([-qmax, qmax], size=(rows, K))
-    else:
-        q = rng.integers(-qmax, qmax + 1, size=(rows, K))
-    if bits == 8:
-        return q.astype(np.int8).view(np.uint8)
-    return ((q[:, 0::2] & 0xF) | ((q[:, 1::2] & 0xF) << 4)).astype(np.uint8)
 
 
 def run_gemm(M, N, K, abits, wbits, seed, bias=False, residual=False, extreme=False, ldy=None, ldr=None):
@@ -97,26 +86,25 @@ def _tile_case(tile, bits):
 
 @pytest.mark.parametrize("tile", TILES)
 @pytest.mark.parametrize("bits", [(8, 8), (4, 4), (8, 4), (4, 8)], ids=lambda b: "A{}W{}".format(*b))
-def test_gemm_every_tile_shape(tile, bits, monkeypatch):
-    """Each tile shape of the MFMA kernel (forced through the FQ_GEMM_TILE test hook)
+def test_gemm_every_tile_shape(tile, bits, hook):
+    """Each tile shape of the MFMA kernel (forced through the gemm_tile test hook)
     on a ragged problem: M and N not multiples of the tile, several k stages."""
-    monkeypatch.setenv("FQ_GEMM_TILE", tile)
+    hook(f"gemm_tile={tile}")
     log(f"gemm tile {tile} bits {bits}")
     _tile_case(tile, bits)
 
 
 @pytest.mark.parametrize("tile", TILES)
-def test_gemm_every_tile_shape_32x32x32_form(tile, monkeypatch):
+def test_gemm_every_tile_shape_32x32x32_form(tile, hook):
     """8-bit x 8-bit codes take v_mfma_i32_16x16x64_i8 by default; the 32x32x32
-    form (FQ_GEMM_MFMA=32 test hook) must give the same exact sums."""
-    monkeypatch.setenv("FQ_GEMM_TILE", tile)
-    monkeypatch.setenv("FQ_GEMM_MFMA", "32")
+    form (gemm_mfma=32 test hook) must give the same exact sums."""
+    hook(f"gemm_tile={tile},gemm_mfma=32")
     log(f"gemm tile {tile} 32x32x32 form")
     _tile_case(tile, (8, 8))
 
 
 @pytest.mark.parametrize("bits", [(8, 8), (4, 4)], ids=lambda b: "A{}W{}".format(*b))
-def test_gemm_two_workgroups_per_cu_many_tiles(bits, monkeypatch):
+def test_gemm_two_workgroups_per_cu_many_tiles(bits, hook):
     """The two-per-CU 64 x 128 tile on 2048 tiles (two workgroups share each
     CU, several waves of them): every int32 sum equals the 128 x 128 tile's
     (the sums do not depend on the tiling), and sampled token rows equal the
@@ -133,7 +121,7 @@ def test_gemm_two_workgroups_per_cu_many_tiles(bits, monkeypatch):
     d_ca, d_cw, d_sa, d_sw = dev(ca), dev(cw), dev(sa), dev(sw)
     out = {}
     for tile in ("64x128x2", "128x128"):
-        monkeypatch.setenv("FQ_GEMM_TILE", tile)
+        hook(f"gemm_tile={tile}")
         y = dev(np.zeros((M, N), np.uint16))
         acc = dev(np.zeros((M, N), np.int32))
         fq_gemm(d_ca, d_sa, M, abits, d_cw, d_sw, N, K, wbits, None, None, N, y, N, acc)
@@ -165,12 +153,12 @@ GEMV_SHAPES = [
 @pytest.mark.parametrize("shape", GEMV_SHAPES, ids=lambda s: "M{}_N{}_K{}".format(*s))
 @pytest.mark.parametrize("bits", [(8, 8), (4, 4), (8, 4), (4, 8)], ids=lambda b: "A{}W{}".format(*b))
 @pytest.mark.parametrize("kernel", ["default", "split"])
-def test_gemv_split_k_shapes(shape, bits, kernel, monkeypatch):
+def test_gemv_split_k_shapes(shape, bits, kernel, hook):
     """Decode-sized M through the default kernel choice and through the split-K
-    kernel forced by the FQ_GEMV=split test hook."""
+    kernel forced by the gemv=split test hook."""
     M, N, K = shape
     if kernel == "split":
-        monkeypatch.setenv("FQ_GEMV", "split")
+        hook("gemv=split")
     log(f"gemv {kernel} M={M} N={N} K={K} A{bits[0]}W{bits[1]}")
     acc, acc_ref, yg, yf, sa, sw, b, res = run_gemm(M, N, K, bits[0], bits[1], seed=M + N + K, bias=True,
                                                     residual=(M % 2 == 0))

@@ -14,7 +14,8 @@ from typing import Optional
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libfq.so")
+# FQ_LIB selects another build of the same library (the host-sanitizer build)
+LIB_PATH = os.environ.get("FQ_LIB") or os.path.join(HERE, "libfq.so")
 
 FQ_OK = 0
 _STATUS = {0: "FQ_OK", 1: "FQ_ERR_ARG", 2: "FQ_ERR_SHAPE", 3: "FQ_ERR_UNSUPPORTED", 4: "FQ_ERR_ALIGN",
@@ -25,6 +26,8 @@ _P, _I32, _I64, _F, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctype
 SIGNATURES = {
     "fq_last_error": ([], ctypes.c_char_p),
     "fq_abi_version": ([], ctypes.c_int),
+    "fq_device_init": ([], ctypes.c_int),
+    "fq_test_hook": ([ctypes.c_char_p], ctypes.c_int),
     "fq_weight_bytes": ([_I32, _I32, _I32], _SZ),
     "fq_act_bytes": ([_I32, _I32, _I32], _SZ),
     "fq_fold_gain": ([_P, _P, _I32, _P], ctypes.c_int),
@@ -81,6 +84,16 @@ def last_error() -> str:
 
 def abi_version() -> int:
     return lib().fq_abi_version()
+
+
+def fq_device_init():
+    """Per-device set-up of the current device (optional; see include/fq.h)."""
+    _check(lib().fq_device_init())
+
+
+def fq_test_hook(spec: Optional[str]):
+    """Force kernel choices for the tests ("gemm_tile=64x128,gemm_mfma=32,gemv=split"; "" resets)."""
+    _check(lib().fq_test_hook(None if spec is None else spec.encode()))
 
 
 # ------------------------------------------------------------------ host entry points

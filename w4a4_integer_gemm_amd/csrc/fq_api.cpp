@@ -6,10 +6,11 @@
 #include <hip/hip_runtime.h>
 
 #include <climits>
-
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
+#include <mutex>
 #include <string>
 
 #include "../../include/fq.h"
@@ -21,6 +22,92 @@ static thread_local std::string g_error;
 
 void set_error(const std::string& msg) { g_error = msg; }
 void clear_error() { g_error.clear(); }
+
+namespace {
+
+// Applies a test-hook spec "key=value,key=value" (keys gemm_tile, gemm_mfma,
+// gemv; "" or "default" resets every hook).  Returns false, with the reason in
+// *why, on an unknown key or value; nothing changes then.
+bool apply_hooks(Hooks& h, const char* spec, std::string* why) {
+    int tile = -1, mfma = 16, split = 0;
+    std::string s = spec ? spec : "";
+    if (s == "default") s.clear();
+    size_t pos = 0;
+    while (pos < s.size()) {
+        size_t end = s.find(',', pos);
+        if (end == std::string::npos) end = s.size();
+        const std::string item = s.substr(pos, end - pos);
+        pos = end + 1;
+        if (item.empty()) continue;
+        const size_t eq = item.find('=');
+        const std::string key = item.substr(0, eq), val = eq == std::string::npos ? "" : item.substr(eq + 1);
+        if (key == "gemm_tile") {
+            tile = val == "auto" ? -1 : gemm_tile_id(val.c_str());
+            if (tile < 0 && val != "auto") {
+                *why = "unknown gemm_tile '" + val + "'";
+                return false;
+            }
+        } else if (key == "gemm_mfma") {
+            if (val != "16" && val != "32") {
+                *why = "gemm_mfma must be 16 or 32, not '" + val + "'";
+                return false;
+            }
+            mfma = val == "16" ? 16 : 32;
+        } else if (key == "gemv") {
+            if (val != "split" && val != "auto") {
+                *why = "gemv must be split or auto, not '" + val + "'";
+                return false;
+            }
+            split = val == "split";
+        } else {
+            *why = "unknown hook '" + key + "' (gemm_tile, gemm_mfma, gemv)";
+            return false;
+        }
+    }
+    h.gemm_tile.store(tile, std::memory_order_relaxed);
+    h.gemm_mfma.store(mfma, std::memory_order_relaxed);
+    h.gemv_split.store(split, std::memory_order_relaxed);
+    return true;
+}
+
+Hooks* make_hooks() {
+    static Hooks h;
+    std::string why;
+    const char* env = std::getenv("FQ_TEST_HOOK");  // read once per process
+    if (env && !apply_hooks(h, env, &why)) std::fprintf(stderr, "libfq: FQ_TEST_HOOK ignored: %s\n", why.c_str());
+    return &h;
+}
+
+DeviceInfo g_devices[kMaxDevices];
+hipError_t g_device_err[kMaxDevices];
+std::once_flag g_device_once[kMaxDevices];
+
+hipError_t init_device(int dev, DeviceInfo& d) {
+    d.device = dev;
+    hipError_t e = hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&d.lds_per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev);
+    if (e == hipSuccess && (d.cus < 1 || d.lds_per_cu < 1)) e = hipErrorInvalidDevice;
+    if (e == hipSuccess) e = init_gemv_device(d);
+    return e;
+}
+
+}  // namespace
+
+Hooks& hooks() {
+    static Hooks* const h = make_hooks();
+    return *h;
+}
+
+hipError_t prepare_device(const DeviceInfo** info) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::call_once(g_device_once[dev], [dev] { g_device_err[dev] = init_device(dev, g_devices[dev]); });
+    if (g_device_err[dev] != hipSuccess) return g_device_err[dev];
+    *info = &g_devices[dev];
+    return hipSuccess;
+}
 
 }  // namespace fq
 
@@ -158,8 +245,13 @@ size_t code_bytes(int32_t rows, int32_t K, int32_t bits) {
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-fq_status run_gemm(const char* fn, const fq::GemmArgs& g, hipStream_t stream) {
-    hipError_t e = g.M <= fq::kGemvMaxM ? fq::launch_gemv(g, stream) : fq::launch_gemm(g, stream);
+// The device set-up every device entry point runs before it queues anything.
+fq_status prepare(const char* fn, const fq::DeviceInfo** info) {
+    return device_status(fn, fq::prepare_device(info));
+}
+
+fq_status run_gemm(const char* fn, const fq::GemmArgs& g, const fq::DeviceInfo& dev, hipStream_t stream) {
+    hipError_t e = g.M <= fq::kGemvMaxM ? fq::launch_gemv(g, dev, stream) : fq::launch_gemm(g, stream);
     return device_status(fn, e);
 }
 
@@ -201,9 +293,24 @@ fq_status fq_prologue(const void* x_bf16, int32_t M, int32_t K, int64_t ldx, con
     const char* fn = "fq_prologue";
     FQ_TRY(validate_prologue(fn, x_bf16, M, K, ldx, gamma_folded, eps, ascale, fold_after, hblock, abits,
                              act_codes, act_scale));
+    const fq::DeviceInfo* dev = nullptr;
+    FQ_TRY(prepare(fn, &dev));
     fq::PrologueArgs a{static_cast<const uint16_t*>(x_bf16), M, K, ldx, gamma_folded, eps, ascale,
                        fold_after, hblock, abits, static_cast<uint8_t*>(act_codes), act_scale};
     return device_status(fn, fq::launch_prologue(a, static_cast<hipStream_t>(stream)));
+}
+
+fq_status fq_device_init(void) {
+    fq::clear_error();
+    const fq::DeviceInfo* dev = nullptr;
+    return prepare("fq_device_init", &dev);
+}
+
+fq_status fq_test_hook(const char* spec) {
+    fq::clear_error();
+    std::string why;
+    if (!fq::apply_hooks(fq::hooks(), spec, &why)) return fail(FQ_ERR_ARG, "fq_test_hook: " + why);
+    return FQ_OK;
 }
 
 }  // extern "C"
@@ -218,11 +325,13 @@ fq_status gemm_impl(const char* fn, const void* act_codes, const float* act_scal
     FQ_TRY(validate_gemm(fn, act_codes, act_scale, M, abits, w_codes, wscale, N, K, wbits, bias, residual_bf16,
                          ldr, y_bf16, ldy, true, head_dim));
     if (acc_i32 && !aligned(acc_i32, 16)) return fail(FQ_ERR_ALIGN, fmt("%s: acc_i32 is not 16-byte aligned", fn));
+    const fq::DeviceInfo* dev = nullptr;
+    FQ_TRY(prepare(fn, &dev));
     fq::GemmArgs g{static_cast<const uint8_t*>(act_codes), act_scale, M, abits,
                    static_cast<const uint8_t*>(w_codes), wscale, N, K, wbits, bias,
                    static_cast<const uint16_t*>(residual_bf16), ldr, static_cast<uint16_t*>(y_bf16), ldy,
                    acc_i32, head_dim};
-    return run_gemm(fn, g, static_cast<hipStream_t>(stream));
+    return run_gemm(fn, g, *dev, static_cast<hipStream_t>(stream));
 }
 
 fq_status linear_impl(const char* fn, const void* x_bf16, int32_t M, int32_t K, int64_t ldx,
@@ -247,6 +356,10 @@ fq_status linear_impl(const char* fn, const void* x_bf16, int32_t M, int32_t K, 
                              scales));
     FQ_TRY(validate_gemm(fn, codes, scales, M, abits, w_codes, wscale, N, K, wbits, bias, residual_bf16, ldr,
                          y_bf16, ldy, true, head_dim));
+    // every host-side step that can fail (the device set-up) runs before the
+    // prologue is queued; after it only the GEMM's launch itself can fail
+    const fq::DeviceInfo* dev = nullptr;
+    FQ_TRY(prepare(fn, &dev));
     hipStream_t s = static_cast<hipStream_t>(stream);
     fq::PrologueArgs a{static_cast<const uint16_t*>(x_bf16), M, K, ldx, gamma_folded, eps, ascale,
                        fold_after, hblock, abits, codes, scales};
@@ -254,7 +367,7 @@ fq_status linear_impl(const char* fn, const void* x_bf16, int32_t M, int32_t K, 
     fq::GemmArgs g{codes, scales, M, abits, static_cast<const uint8_t*>(w_codes), wscale, N, K, wbits, bias,
                    static_cast<const uint16_t*>(residual_bf16), ldr, static_cast<uint16_t*>(y_bf16), ldy,
                    nullptr, head_dim};
-    return run_gemm(fn, g, s);
+    return run_gemm(fn, g, *dev, s);
 }
 
 }  // namespace
@@ -304,6 +417,8 @@ fq_status fq_geglu(const void* gateup_bf16, int32_t M, int32_t F, int64_t ld_in,
     if (ld_out % 8) return fail(FQ_ERR_ALIGN, fmt("%s: ld_out=%lld is not a multiple of 8 bf16", fn, (long long)ld_out));
     if (!aligned(gateup_bf16, 16)) return fail(FQ_ERR_ALIGN, "fq_geglu: gateup_bf16 is not 16-byte aligned");
     if (!aligned(h_bf16, 16)) return fail(FQ_ERR_ALIGN, "fq_geglu: h_bf16 is not 16-byte aligned");
+    const fq::DeviceInfo* dev = nullptr;
+    FQ_TRY(prepare(fn, &dev));
     return device_status(fn, fq::launch_geglu(static_cast<const uint16_t*>(gateup_bf16), M, F, ld_in,
                                               static_cast<uint16_t*>(h_bf16), ld_out,
                                               static_cast<hipStream_t>(stream)));

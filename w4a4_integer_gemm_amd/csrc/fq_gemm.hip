@@ -36,7 +36,6 @@
 // 8-bit partner permutes its bytes into the nibble order of fq_device.h.
 #include <hip/hip_runtime.h>
 
-#include <cstdlib>
 #include <cstring>
 #include <type_traits>
 
@@ -782,15 +781,12 @@ constexpr int ring_depth() {
 }
 
 // MFMA form: v_mfma_i32_16x16x64_i8 (rows in fragments of 16, so a 144-row
-// tile computes no padding rows) unless the test hook FQ_GEMM_MFMA=32 asks for
+// tile computes no padding rows) unless the test hook gemm_mfma=32 asks for
 // v_mfma_i32_32x32x32_i8.  The 16x16x64 form measured 6-7 % faster on the
 // W8A8 qkv and down layers (22.8 against 24.6 us, 73.9 against 79.1 us), also
 // where no rows are padded: with random operands it sustains a higher rate
 // under the power limit (3.4-3.6 against 3.2-3.3 POP/s).
-int mfma_form() {
-    const char* e = std::getenv("FQ_GEMM_MFMA");
-    return e ? std::atoi(e) : 16;
-}
+int mfma_form() { return hooks().gemm_mfma.load(std::memory_order_relaxed); }
 
 template <int ABITS, int WBITS, int BM, int BNS, bool TWO = false>
 hipError_t launch_shape(const GemmArgs& g, hipStream_t st) {
@@ -882,19 +878,17 @@ int choose_tile(int M, int N, int frag_rows, bool four_bit, bool two_per_cu) {
     return best;
 }
 
-// Test hook: FQ_GEMM_TILE=<name> forces one tile shape (read at every launch).
-int tile_override() {
-    const char* e = std::getenv("FQ_GEMM_TILE");
-    if (!e) return -1;
+}  // namespace
+
+int gemm_tile_id(const char* name) {
     for (int i = 0; i < kNumTiles; ++i)
-        if (std::strcmp(e, kTileNames[i]) == 0) return i;
+        if (std::strcmp(name, kTileNames[i]) == 0) return i;
     return -1;
 }
 
-}  // namespace
-
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream) {
-    int tile = tile_override();
+    // test hook gemm_tile=<name> forces one tile shape
+    int tile = hooks().gemm_tile.load(std::memory_order_relaxed);
     if (tile < 0)
         tile = choose_tile(g.M, g.N, g.abits == 8 && g.wbits == 8 && mfma_form() == 16 ? 16 : 32,
                            g.abits == 4 || g.wbits == 4, g.abits == g.wbits);

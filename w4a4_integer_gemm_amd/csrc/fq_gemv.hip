@@ -16,10 +16,6 @@
 // per tile runs the epilogue.
 #include <hip/hip_runtime.h>
 
-#include <atomic>
-#include <cstdlib>
-#include <cstring>
-
 #include "fq_device.h"
 #include "fq_internal.h"
 
@@ -396,73 +392,81 @@ __global__ __launch_bounds__(64 * kStreamWaves) __attribute__((amdgpu_waves_per_
     }
 }
 
-int device_cus() {
-    static std::atomic<int> cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    int n = cache[dev].load(std::memory_order_relaxed);
-    if (n == 0) {
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-        cache[dev].store(n, std::memory_order_relaxed);
-    }
-    return n;
-}
-
 int stream_mt(int M) { return M <= 16 ? 1 : 2; }
 
 bool stream_fits(const GemmArgs& g) {
     if (g.M < kStreamMinM || g.M > kGemvMaxM) return false;
-    const char* e = std::getenv("FQ_GEMV");  // test hook: "split" keeps the split-K kernel
-    if (e && std::strcmp(e, "split") == 0) return false;
+    if (hooks().gemv_split.load(std::memory_order_relaxed)) return false;  // test hook gemv=split
     return stream_lds_bytes(stream_mt(g.M), act_pitch(g.K * g.abits / 8)) <= size_t(kMaxLds);
 }
 
+int mix_index(int abits, int wbits) { return abits == 8 ? (wbits == 8 ? 0 : 2) : (wbits == 4 ? 1 : 3); }
+
 template <int ABITS, int WBITS, int MT>
-hipError_t launch_stream_t(const GemmArgs& g, hipStream_t st) {
+hipError_t launch_stream_t(const GemmArgs& g, const DeviceInfo& dev, hipStream_t st) {
     const int pitch = act_pitch(g.K * ABITS / 8);
     const size_t lds = stream_lds_bytes(MT, pitch);
-    const auto kern = stream_kernel<ABITS, WBITS, MT>;
-    // resident workgroups per CU for the last LDS size (the codes' share changes with K)
-    static std::atomic<int64_t> occ{-1};
-    int64_t o = occ.load(std::memory_order_relaxed);
-    int per_cu;
-    if (o >= 0 && (o >> 8) == int64_t(lds)) {
-        per_cu = int(o & 0xFF);
-    } else {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
-        if (e != hipSuccess) return e;
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * kStreamWaves, lds);
-        if (e != hipSuccess) return e;
-        if (per_cu < 1) return hipErrorInvalidValue;
-        per_cu = per_cu > 255 ? 255 : per_cu;
-        occ.store((int64_t(lds) << 8) | per_cu, std::memory_order_relaxed);
-    }
-    const int cus = device_cus();
-    if (cus < 1) return hipErrorInvalidDevice;
+    // resident workgroups per CU: the register-limited count (from the device's
+    // set-up) or what the CU's LDS holds, whichever is smaller.  The kernel is
+    // correct for any grid; this only sizes it to one round of residents.
+    int per_cu = dev.stream_regs_wg[mix_index(ABITS, WBITS)][MT - 1];
+    const int by_lds = int(size_t(dev.lds_per_cu) / lds);
+    per_cu = per_cu < by_lds ? per_cu : by_lds;
+    per_cu = per_cu < 1 ? 1 : per_cu;
     const int groups = (g.N + 15) / 16;
-    const int grid = groups < per_cu * cus ? groups : per_cu * cus;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * kStreamWaves), lds, st, g, pitch, groups);
+    const int grid = groups < per_cu * dev.cus ? groups : per_cu * dev.cus;
+    hipLaunchKernelGGL((stream_kernel<ABITS, WBITS, MT>), dim3(grid), dim3(64 * kStreamWaves), lds, st, g, pitch,
+                       groups);
     return hipGetLastError();
 }
 
 template <int ABITS, int WBITS>
-hipError_t launch_stream_bits(const GemmArgs& g, hipStream_t st) {
-    return stream_mt(g.M) == 1 ? launch_stream_t<ABITS, WBITS, 1>(g, st) : launch_stream_t<ABITS, WBITS, 2>(g, st);
+hipError_t launch_stream_bits(const GemmArgs& g, const DeviceInfo& dev, hipStream_t st) {
+    return stream_mt(g.M) == 1 ? launch_stream_t<ABITS, WBITS, 1>(g, dev, st)
+                               : launch_stream_t<ABITS, WBITS, 2>(g, dev, st);
 }
 
-hipError_t launch_stream(const GemmArgs& g, hipStream_t st) {
-    if (g.abits == 8 && g.wbits == 8) return launch_stream_bits<8, 8>(g, st);
-    if (g.abits == 4 && g.wbits == 4) return launch_stream_bits<4, 4>(g, st);
-    if (g.abits == 8 && g.wbits == 4) return launch_stream_bits<8, 4>(g, st);
-    return launch_stream_bits<4, 8>(g, st);
+hipError_t launch_stream(const GemmArgs& g, const DeviceInfo& dev, hipStream_t st) {
+    if (g.abits == 8 && g.wbits == 8) return launch_stream_bits<8, 8>(g, dev, st);
+    if (g.abits == 4 && g.wbits == 4) return launch_stream_bits<4, 4>(g, dev, st);
+    if (g.abits == 8 && g.wbits == 4) return launch_stream_bits<8, 4>(g, dev, st);
+    return launch_stream_bits<4, 8>(g, dev, st);
+}
+
+// The streaming kernels' part of a device's set-up: raise the dynamic-LDS
+// limit and record the register-limited residency (dynamic LDS 0).
+template <int ABITS, int WBITS, int MT>
+hipError_t init_stream_kernel(DeviceInfo& d) {
+    const void* kern = reinterpret_cast<const void*>(stream_kernel<ABITS, WBITS, MT>);
+    hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
+    if (e != hipSuccess) return e;
+    int n = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, stream_kernel<ABITS, WBITS, MT>, 64 * kStreamWaves, 0);
+    if (e != hipSuccess) return e;
+    if (n < 1) return hipErrorInvalidValue;
+    d.stream_regs_wg[mix_index(ABITS, WBITS)][MT - 1] = n;
+    return hipSuccess;
+}
+
+template <int ABITS, int WBITS>
+hipError_t init_stream_bits(DeviceInfo& d) {
+    const hipError_t e = init_stream_kernel<ABITS, WBITS, 1>(d);
+    return e != hipSuccess ? e : init_stream_kernel<ABITS, WBITS, 2>(d);
 }
 
 }  // namespace
 
-hipError_t launch_gemv(const GemmArgs& g, hipStream_t stream) {
+hipError_t init_gemv_device(DeviceInfo& d) {
+    hipError_t e = init_stream_bits<8, 8>(d);
+    if (e == hipSuccess) e = init_stream_bits<4, 4>(d);
+    if (e == hipSuccess) e = init_stream_bits<8, 4>(d);
+    if (e == hipSuccess) e = init_stream_bits<4, 8>(d);
+    return e;
+}
+
+hipError_t launch_gemv(const GemmArgs& g, const DeviceInfo& dev, hipStream_t stream) {
     if (g.M > kGemvMaxM) return hipErrorInvalidValue;
-    if (stream_fits(g)) return launch_stream(g, stream);
+    if (stream_fits(g)) return launch_stream(g, dev, stream);
     if (g.abits == 8 && g.wbits == 8)
         launch_bits<8, 8>(g, stream);
     else if (g.abits == 4 && g.wbits == 4)

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <string>
 
 namespace fq {
@@ -52,10 +53,41 @@ __host__ __device__ inline uint16_t* out_ptr(const GemmArgs& g, int m, int n) {
     return g.y + int64_t(m) * g.ldy + n;
 }
 
-// Enqueue the kernels; they return hipGetLastError() of the launch.
+// Forced kernel choices for the tests (fq_test_hook, or the FQ_TEST_HOOK
+// environment variable read once, at the first use).  The launch paths read
+// these with relaxed atomic loads; nothing on them calls getenv.
+struct Hooks {
+    std::atomic<int> gemm_tile{-1};  // -1: the cost model picks; else a tile id of fq_gemm.hip
+    std::atomic<int> gemm_mfma{16};  // 16: v_mfma_i32_16x16x64_i8 where it applies; 32: 32x32x32 only
+    std::atomic<int> gemv_split{0};  // 1: decode-sized M always takes the split-K GEMV
+};
+Hooks& hooks();
+// Tile id of a tile name ("128x144", ...), or -1 (fq_gemm.hip).
+int gemm_tile_id(const char* name);
+
+// What a device's launches need to know, gathered once per device and process
+// by prepare_device (fq_api.cpp): the compute-unit count, the LDS of a CU and,
+// per streaming-GEMV kernel (bit mix x token tiles), how many of its
+// workgroups the register file lets a CU hold.  The same set-up raises those
+// kernels' dynamic-LDS limit, so no launch makes a HIP call other than the
+// launch itself.
+constexpr int kMaxDevices = 64;
+struct DeviceInfo {
+    int device;
+    int cus;
+    int lds_per_cu;
+    int stream_regs_wg[4][2];  // [bit mix: 8/8, 4/4, 8/4, 4/8][token tiles - 1]
+};
+// Set-up of the current device (once); *info points at its record.
+hipError_t prepare_device(const DeviceInfo** info);
+// The streaming GEMV's part of that set-up (fq_gemv.hip).
+hipError_t init_gemv_device(DeviceInfo& d);
+
+// Enqueue the kernels; they return hipGetLastError() of the launch.  Shapes
+// are validated by the caller; a launch makes no other HIP call.
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t stream);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
-hipError_t launch_gemv(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_gemv(const GemmArgs& a, const DeviceInfo& dev, hipStream_t stream);
 hipError_t launch_geglu(const uint16_t* gu, int32_t M, int32_t F, int64_t ld_in, uint16_t* h, int64_t ld_out,
                         hipStream_t stream);
 

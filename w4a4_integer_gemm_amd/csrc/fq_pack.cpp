@@ -11,6 +11,7 @@
 // scales by 1/sqrt(b).  Codes round half-to-even against the stored float32
 // scale s_n = (float)(max|u_n| / qmax) and clamp to +-qmax.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -147,19 +148,42 @@ fq_status check_rows(const char* fn, int32_t N, int32_t K, const float* ascale, 
     return FQ_OK;
 }
 
-// Runs rows [0, N) of `fn(n0, n1)` on up to 16 host threads.
+// Runs rows [0, N) of `fn(n0, n1)` on up to 16 host threads.  No exception
+// leaves it: a range whose thread cannot be started runs on the calling
+// thread, and a range that throws (an allocation failure) is reported by the
+// false return.
 template <class F>
-void parallel_rows(int32_t N, F fn) {
+bool parallel_rows(int32_t N, F fn) {
+    std::atomic<bool> ok{true};
+    auto run = [&](int32_t n0, int32_t n1) {
+        try {
+            fn(n0, n1);
+        } catch (...) {
+            ok.store(false);
+        }
+    };
     unsigned nt = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
     nt = std::min<unsigned>(nt, unsigned(N));
     std::vector<std::thread> pool;
+    try {
+        pool.reserve(nt);
+    } catch (...) {
+        nt = 1;
+    }
     const int32_t per = (N + int32_t(nt) - 1) / int32_t(nt);
-    for (unsigned t = 0; t < nt; ++t) {
+    // range t = rows [t per, (t + 1) per); the calling thread takes range 0
+    for (unsigned t = 1; t < nt; ++t) {
         const int32_t n0 = int32_t(t) * per, n1 = std::min(N, n0 + per);
         if (n0 >= n1) break;
-        pool.emplace_back(fn, n0, n1);
+        try {
+            pool.emplace_back(run, n0, n1);
+        } catch (...) {
+            run(n0, n1);
+        }
     }
+    run(0, std::min(N, per));
     for (auto& th : pool) th.join();
+    return ok.load();
 }
 
 }  // namespace
@@ -174,9 +198,10 @@ extern "C" fq_status fq_pack_weights(const float* W, int32_t N, int32_t K, const
     if (!W || !codes_out || !wscale_out) return fail(FQ_ERR_ARG, "fq_pack_weights: W, codes_out or wscale_out is NULL");
     const fq_status st = check_rows("fq_pack_weights", N, K, ascale, fold_after, hblock, wbits);
     if (st != FQ_OK) return st;
-    parallel_rows(N, [&](int32_t n0, int32_t n1) {
-        pack_rows(W, n0, n1, K, ascale, fold_after, hblock, wbits, static_cast<uint8_t*>(codes_out), wscale_out);
-    });
+    if (!parallel_rows(N, [&](int32_t n0, int32_t n1) {
+            pack_rows(W, n0, n1, K, ascale, fold_after, hblock, wbits, static_cast<uint8_t*>(codes_out), wscale_out);
+        }))
+        return fail(FQ_ERR_ARG, "fq_pack_weights: host memory for the row buffers could not be allocated");
     return FQ_OK;
 }
 
@@ -197,8 +222,12 @@ extern "C" fq_status fq_dequant_rows(const void* codes, const float* wscale, int
             fq::set_error(buf);
             return FQ_ERR_ARG;
         }
-    parallel_rows(N, [&](int32_t n0, int32_t n1) {
-        dequant_rows(static_cast<const uint8_t*>(codes), wscale, n0, n1, K, ascale, fold_after, hblock, wbits, W_out);
-    });
+    if (!parallel_rows(N, [&](int32_t n0, int32_t n1) {
+            dequant_rows(static_cast<const uint8_t*>(codes), wscale, n0, n1, K, ascale, fold_after, hblock, wbits,
+                         W_out);
+        })) {
+        fq::set_error("fq_dequant_rows: host memory for the row buffers could not be allocated");
+        return FQ_ERR_ARG;
+    }
     return FQ_OK;
 }
