@@ -9,9 +9,12 @@ already resident in HBM when the timed region starts.
 
 Prints ONE JSON line: throughput in TOPS (2*M*N*K integer ops per step), the
 roofline of the dominant kernel (the MFMA GEMM, timed with HIP events on the
-stream it runs on), the CPU oracle timed on the host, and secondary lines for
-the other prefill shape (MLP down projection with residual) and the decode
-GEMV (GB/s, weights rotated over copies larger than the 256 MB Infinity Cache).
+stream it runs on), the CPU oracle timed on the host, secondary lines for the
+other prefill shape (MLP down projection with residual), the W4A4 sites and
+the decode GEMV (GB/s, weights rotated over copies larger than the 256 MB
+Infinity Cache), the measured MFMA-i8 and HBM-read ceilings of this GPU next
+to the datasheet peaks, and amd-smi clocks and power (idle before, under
+load, after).
 """
 from __future__ import annotations
 
@@ -156,7 +159,8 @@ def bench_prefill(name, steps, warmup):
     site.linear(x, residual=res, y=y)
     torch.cuda.synchronize()
     ok, detail = parity(wl, site, y, codes, scales)
-    return dict(wl=wl, ms=ms, tops=ops / (ms * 1e-3) / 1e12, ms_prologue=ms_pro, ms_gemm=ms_gemm, ms_graph=ms_graph,
+    return dict(wl=wl, site=site, step=step, ms=ms, tops=ops / (ms * 1e-3) / 1e12, ms_prologue=ms_pro,
+                ms_gemm=ms_gemm, ms_graph=ms_graph,
                 warmup_run=nwarm,
                 tops_graph=ops / (ms_graph * 1e-3) / 1e12,
                 gemm_tops=ops / (ms_gemm * 1e-3) / 1e12, parity=detail, parity_ok=ok, ops=ops, batches=batches)
@@ -245,7 +249,7 @@ def cpu_baseline(name, min_seconds=10.0, max_reps=400):
             break
     t = float(np.median(times))
     ops = 2.0 * wl.M * wl.N * wl.K
-    out = dict(value=ops / t / 1e12, unit="TOPS", cores=oracle.num_threads(), kind="oracle",
+    out = dict(value=ops / t / 1e12, unit="TOP/s", cores=oracle.num_threads(), cpu_model=cpu_model(), kind="oracle",
                sample=f"whole {name} fq_linear (M={wl.M} K={wl.K} N={wl.N}) on the oracle, "
                       f"{len(times)} repetitions ({sum(times):.1f} s), median {t * 1e3:.1f} ms; weights packed once")
     out["one_core"] = cpu_one_core(name)
@@ -265,7 +269,7 @@ while time.perf_counter() - t_start < {seconds} or len(ts) < 2:
     oracle.linear(wl, codes_w=codes_w, wscale=wscale)
     ts.append(time.perf_counter() - t0)
 t = float(np.median(ts))
-print(json.dumps(dict(value=2.0 * wl.M * wl.N * wl.K / t / 1e12, unit="TOPS", cores=oracle.num_threads(),
+print(json.dumps(dict(value=2.0 * wl.M * wl.N * wl.K / t / 1e12, unit="TOP/s", cores=oracle.num_threads(),
                       sample=f"{{wl.M}} tokens of {name} (K={{wl.K}} N={{wl.N}}), {{len(ts)}} repetitions, "
                              f"median {{t * 1e3:.1f}} ms")))
 """
@@ -321,6 +325,175 @@ def load_traffic(kernel_key, sources):
     return e["bytes"] if h.hexdigest() == e.get("source_sha256") else None
 
 
+CEILING_LIB = os.path.join(ROOT, "w4a4_integer_gemm_amd", "libfq_ceiling.so")
+
+
+def _ceiling_lib():
+    import ctypes
+    if not os.path.exists(CEILING_LIB):
+        raise RuntimeError(f"{CEILING_LIB} not found; build it with `python w4a4_integer_gemm_amd/build.py`")
+    L = ctypes.CDLL(CEILING_LIB)
+    P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    L.fqc_mfma_i8.argtypes = [P, I64, I32, I32, P, P]
+    L.fqc_mfma_i8.restype = ctypes.c_int
+    L.fqc_mfma_i8_ops.argtypes = [I32, I32]
+    L.fqc_mfma_i8_ops.restype = I64
+    L.fqc_stream_read.argtypes = [P, I64, I32, I32, P, P]
+    L.fqc_stream_read.restype = ctypes.c_int
+    return L
+
+
+def _event_ms(run, reps):
+    """Mean ms of `reps` back-to-back run() calls, HIP events on the current stream."""
+    import torch
+    s = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(s)
+    for _ in range(reps):
+        run()
+    b.record(s)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def measure_ceilings(stream_bytes=135_790_592, copies=5):
+    """Measured ceilings of this part, next to the datasheet peaks:
+    - the v_mfma_i32_16x16x64_i8 rate on random operand bytes (the codes' power
+      draw) and on zero bytes, one and two waves per SIMD;
+    - the HBM read rate of a plain grid-stride read of `copies` rotated buffers
+      of the decode layer's weight size (37888 x 3584 bytes), best over the
+      launch shapes swept."""
+    import torch
+    L = _ceiling_lib()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = torch.cuda.current_stream().cuda_stream
+    out = torch.zeros(4, dtype=torch.int32, device="cuda")
+    res = {"mfma_i8": {}, "stream_read": {}}
+    iters = 4000
+    best_rand = 0.0
+    for kind in ("random", "zero"):
+        for per_cu in (1, 2):
+            blocks = cus * per_cu
+            n16 = blocks * 256 * 16
+            src = (torch.randint(-128, 128, (n16 * 16,), dtype=torch.int8, device="cuda") if kind == "random"
+                   else torch.zeros(n16 * 16, dtype=torch.int8, device="cuda"))
+            run = lambda: L.fqc_mfma_i8(src.data_ptr(), n16, blocks, iters, out.data_ptr(), stream)
+            rc = run()
+            if rc != 0:
+                raise RuntimeError(f"fqc_mfma_i8 failed: hip error {rc}")
+            t0 = time.perf_counter()
+            while time.perf_counter() - t0 < WARM_MS * 1e-3 * 4:  # settle the clock under this load
+                run()
+                torch.cuda.synchronize()
+            ms = _event_ms(run, 5)
+            tops = L.fqc_mfma_i8_ops(blocks, iters) / (ms * 1e-3) / 1e12
+            res["mfma_i8"][f"{kind}_{per_cu}wave_per_simd"] = tops
+            if kind == "random":
+                best_rand = max(best_rand, tops)
+            del src
+    res["mfma_i8_random_tops"] = best_rand
+    n16 = stream_bytes // 16
+    bufs = [torch.randint(-128, 128, (stream_bytes,), dtype=torch.int8, device="cuda") for _ in range(copies)]
+    best = (0.0, None)
+    for per_cu in (4, 8, 16):
+        for u in (4, 8, 16):
+            i = [0]
+
+            def run():
+                L.fqc_stream_read(bufs[i[0] % copies].data_ptr(), n16, cus * per_cu, u, out.data_ptr(), stream)
+                i[0] += 1
+            for _ in range(20):
+                run()
+            ms = _event_ms(run, 50)
+            gbs = n16 * 16 / (ms * 1e-3) / 1e9
+            res["stream_read"][f"{per_cu}wg_per_cu_u{u}"] = gbs
+            if gbs > best[0]:
+                best = (gbs, f"{cus * per_cu} workgroups of 256, {u} x 16-byte loads in flight per lane")
+    res["stream_read_gbs"] = best[0]
+    res["stream_read_config"] = best[1]
+    res["stream_read_buffers"] = f"{copies} rotated buffers of {stream_bytes} bytes"
+    del bufs
+    torch.cuda.empty_cache()
+    return res
+
+
+def _smi_value(v):
+    if isinstance(v, dict):
+        v = v.get("value", None)
+    try:
+        return float(v)
+    except (TypeError, ValueError):
+        return None
+
+
+def amd_smi_sample():
+    """Current gfx and memory clocks (MHz) and socket power (W) of GPU 0 from
+    amd-smi, or None when amd-smi is unavailable."""
+    import subprocess
+    try:
+        p = subprocess.run(["amd-smi", "metric", "-g", "0", "-p", "-c", "--json"], capture_output=True, text=True,
+                           timeout=30)
+        data = json.loads(p.stdout)
+    except (OSError, subprocess.SubprocessError, ValueError):
+        return None
+    if isinstance(data, list):
+        data = data[0] if data else {}
+    if isinstance(data, dict) and "gpu_data" in data:
+        data = data["gpu_data"][0] if data["gpu_data"] else {}
+    clk = data.get("clock", {}) if isinstance(data, dict) else {}
+    pw = data.get("power", {}) if isinstance(data, dict) else {}
+    gfx = [_smi_value(c.get("clk")) for k, c in sorted(clk.items()) if k.startswith("gfx_") and isinstance(c, dict)]
+    gfx = [g for g in gfx if g is not None]
+    mem = _smi_value(clk.get("mem_0", {}).get("clk")) if isinstance(clk.get("mem_0"), dict) else None
+    return {"sclk_mhz": (sum(gfx) / len(gfx)) if gfx else None, "sclk_per_xcd_mhz": gfx or None, "mclk_mhz": mem,
+            "socket_power_w": _smi_value(pw.get("socket_power"))}
+
+
+def sample_under_load(step, seconds=1.5):
+    """amd-smi sampled from a helper thread while step() runs back to back."""
+    import threading
+    import torch
+    box = {}
+    th = threading.Thread(target=lambda: box.update(s=amd_smi_sample()))
+    t0 = time.perf_counter()
+    th.start()
+    while th.is_alive() or time.perf_counter() - t0 < seconds:
+        for _ in range(50):
+            step()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 > 60:
+            break
+    th.join()
+    return box.get("s")
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or None
+
+
+WORKLOAD_DESC = {
+    "qkv_w8a8": "Qwen2.5-7B-shaped fused QKV projection",
+    "down_w8a8": "Qwen2.5-7B-shaped MLP down projection with the residual",
+    "gateup_w4a4": "Gemma-2B-shaped MLP gate+up projection",
+    "down_w4a4": "Gemma-2B-shaped MLP down projection with the residual",
+    "tiny_w8a8": "tiny 16-token site",
+    "decode_m1_w8a8": "decode GEMV (fused gate+up), 1 token",
+    "decode_m16_w8a8": "decode GEMV (fused gate+up), 16 tokens",
+}
+
+
+def describe(name, wl):
+    return (f"{name}: {WORKLOAD_DESC.get(name, name)}, M={wl.M} K={wl.K} N={wl.N} W{wl.wbits}A{wl.abits} "
+            f"hblock={wl.hblock}, weights warm in HBM")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -331,6 +504,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one 256 MiB elementwise copy kernel (scale for HBM byte counters)")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the measured MFMA and HBM-read ceilings")
+    ap.add_argument("--no-clocks", action="store_true", help="skip the amd-smi clock and power samples")
+    ap.add_argument("--ceilings-only", action="store_true", help="print the measured ceilings only")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} requested, but this build measures one GPU only: the FoldQuant "
@@ -343,12 +519,20 @@ def main():
         sys.exit(1)
     import w4a4_integer_gemm_amd as fq
     fq.lib()  # fail loudly if the HIP library is missing
+    if args.ceilings_only:
+        print(json.dumps({"ceilings": measure_ceilings()}), flush=True)
+        return
 
+    clocks = {}
+    if not args.no_clocks:
+        clocks["idle_before"] = amd_smi_sample()
     r = bench_prefill(args.workload, args.steps, args.warmup)
     wl = r["wl"]
     achieved = r["ops"] / (r["ms_gemm"] * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "kernel": "gemm_kernel<8,8> (fq_gemm, MFMA i8)", "achieved": achieved,
-                "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_INT8_TOPS,
+    roofline = {"bound": "mfma", "kernel": f"gemm_kernel<{wl.abits},{wl.wbits}> (fq_gemm, MFMA i8)",
+                "achieved": achieved, "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
+                "unit_note": "tera integer operations per second (2*M*N*K per GEMM)",
+                "frac": achieved / PEAK_INT8_TOPS,
                 "traffic": load_traffic(f"gemm:{args.workload}", ("fq_gemm.hip", "fq_device.h")),
                 "traffic_unit": "bytes per launch (scaled FETCH_SIZE + WRITE_SIZE)",
                 "algorithmic_bytes": gemm_bytes(wl)}
@@ -381,6 +565,22 @@ def main():
                               "ms_gemv": d["ms_gemv"], "algorithmic_bytes": d["bytes"],
                               "weights": "rotated over 5 device copies (679 MB) to defeat the Infinity Cache"})
         torch.cuda.empty_cache()
+    ceilings = None if args.no_ceilings else measure_ceilings()
+    if ceilings:
+        mf, sr = ceilings["mfma_i8_random_tops"], ceilings["stream_read_gbs"]
+        roofline["measured_peak"] = mf
+        roofline["frac_of_measured"] = achieved / mf
+        roofline["measured_peak_note"] = "v_mfma_i32_16x16x64_i8 back to back on random operand bytes, this GPU"
+        for e in secondary:
+            if e.get("metric") == "decode GB/s":
+                e["frac_measured_read"] = e["value"] / sr
+                e["gemv_frac_measured_read"] = e["gemv_gbs"] / sr
+            elif e.get("metric") == "fq_linear TOPS":
+                e["frac_measured_mfma"] = e["value"] / mf
+    if not args.no_clocks:
+        clocks["under_load"] = sample_under_load(r["step"])
+        clocks["under_load_note"] = f"sampled while {args.workload} fq_linear ran back to back"
+        clocks["after"] = amd_smi_sample()
     probe = copy_probe() if args.copy_probe else None
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.workload)
     out = {
@@ -396,10 +596,9 @@ def main():
         "vs_baseline": None,
         "dtype": "i8",
         "data": "synthetic",
-        "config": {"workload": f"{args.workload}: fused QKV projection M={wl.M} K={wl.K} N={wl.N} "
-                               f"W{wl.wbits}A{wl.abits} hblock={wl.hblock}, weights warm in HBM",
-                   "global_batch": wl.M, "parallelism": "single GPU"},
+        "config": {"workload": describe(args.workload, wl), "global_batch": wl.M, "parallelism": "single GPU"},
         "frac_int8_peak": r["tops"] / PEAK_INT8_TOPS,
+        "frac_measured_mfma": (r["tops"] / ceilings["mfma_i8_random_tops"]) if ceilings else None,
         "timing": "value: the calls launched back to back from Python; 'graph': the same calls replayed from HIP "
                   "graphs of 20 (no launch gaps; the large kernels then run slower); ms_prologue, ms_gemm "
                   "and the roofline: one kernel replayed from graphs",
@@ -412,6 +611,8 @@ def main():
         "parity": r["parity"],
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "ceilings": ceilings,
+        "clocks": clocks or None,
         "secondary": secondary,
     }
     if probe:

@@ -44,9 +44,10 @@ def lib():
     """Load (building first if absent) the oracle shared library."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB):
+        path = os.environ.get("FQO_LIB") or LIB  # FQO_LIB: the host-sanitizer build of the oracle
+        if path == LIB and not os.path.exists(LIB):
             build()
-        L = ctypes.CDLL(LIB)
+        L = ctypes.CDLL(path)
         L.fqo_hadamard_entry.argtypes = [_I32, _I32, _I32]
         L.fqo_rotate_f64.argtypes = [_P, _I64, _I32]
         L.fqo_butterfly_f32.argtypes = [_P, _I64, _I32]
