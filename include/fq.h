@@ -43,7 +43,8 @@
  *     a record made once per process on the first device call there (or by
  *     fq_device_init): the compute-unit and LDS sizes, and the streaming
  *     GEMV kernels' register-limited residency after raising their
- *     dynamic-LDS limit; and the process-wide test hooks (fq_test_hook).
+ *     dynamic-LDS limit, and the address of its fq_linear_noalloc scratch
+ *     array; and the process-wide test hooks (fq_test_hook).
  *     No call depends on an earlier call's data.
  *   - Device entry points are asynchronous on `stream` (a hipStream_t passed as
  *     void*; NULL is the null stream) and take device pointers.
@@ -193,6 +194,27 @@ fq_status fq_linear(const void* x_bf16, int32_t M, int32_t K, int64_t ldx,
                     const float* bias, const void* residual_bf16, int64_t ldr,
                     void* y_bf16, int64_t ldy,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* fq_linear without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid allocation).  The codes and scales that pass from the prologue
+ * to the GEMM live in a fixed device array of the library, one per GPU,
+ * created when the library's code is loaded on that GPU and held until the
+ * process ends; its size is fq_linear_noalloc_max_bytes() (24 MiB), and a
+ * call needing more than fq_linear_workspace_bytes(M, K, abits) allows
+ * returns FQ_ERR_UNSUPPORTED before any work.  The call allocates nothing
+ * (no hipMalloc, no allocating library routine) and clears nothing: the
+ * prologue overwrites every byte the GEMM then reads.  All calls on one GPU
+ * share that GPU's array, so calls that may overlap on one GPU (other
+ * streams, other threads) race and must be ordered by the caller.  Other
+ * arguments, results and errors as in fq_linear. */
+fq_status fq_linear_noalloc(const void* x_bf16, int32_t M, int32_t K, int64_t ldx,
+                            const float* gamma_folded, float eps, const float* ascale,
+                            int32_t fold_after, int32_t hblock, int32_t abits,
+                            const void* w_codes, const float* wscale, int32_t N, int32_t wbits,
+                            const float* bias, const void* residual_bf16, int64_t ldr,
+                            void* y_bf16, int64_t ldy, void* stream);
+size_t fq_linear_noalloc_max_bytes(void);
 
 /* GeGLU between the sites of a chained MLP block (gate+up site -> GeGLU -> down
  * site with the residual, the Gemma-style MLP of the page's pi0.5 backbone):

@@ -307,3 +307,25 @@ def test_test_hook_parses_and_rejects():
         assert L.fq_test_hook(bad.encode()) == 1, bad
         assert what in _binding.last_error(), _binding.last_error()
     assert L.fq_test_hook(b"") == 0
+
+
+def test_linear_noalloc_rejects_before_device_work():
+    """fq_linear_noalloc refuses a workspace larger than its scratch array (and
+    the usual bad arguments) before it touches the device."""
+    L = _binding.lib()
+    cap = L.fq_linear_noalloc_max_bytes()
+    assert cap == 24 << 20
+    # 2048 tokens x 16384 8-bit codes = 32 MiB of codes > 24 MiB
+    rc = L.fq_linear_noalloc(DEV, 2048, 16384, 16384, None, 1e-6, None, 0, 128, 8, DEV, DEV, 512, 8, None, None, 0,
+                             DEV, 512, None)
+    assert rc == 3 and "scratch array" in _binding.last_error() and "fq_linear" in _binding.last_error()
+    assert L.fq_linear_workspace_bytes(2048, 16384, 8) > cap
+    rc = L.fq_linear_noalloc(DEV, 16, 3584, 3584, None, 1e-6, None, 0, 100, 8, DEV, DEV, 512, 8, None, None, 0,
+                             DEV, 512, None)
+    assert rc == 2 and "hblock" in _binding.last_error()
+    rc = L.fq_linear_noalloc(DEV, 16, 3584, 3584, None, 1e-6, None, 0, 128, 8, DEV, DEV, 500, 8, None, None, 0,
+                             DEV, 512, None)
+    assert rc == 2 and "N=500" in _binding.last_error()
+    rc = L.fq_linear_noalloc(BAD, 16, 3584, 3584, None, 1e-6, None, 0, 128, 8, DEV, DEV, 512, 8, None, None, 0,
+                             DEV, 512, None)
+    assert rc == 4 and "x_bf16" in _binding.last_error()

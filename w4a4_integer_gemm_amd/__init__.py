@@ -7,13 +7,14 @@ memory and streams.
 """
 from ._binding import (FqError, abi_version, fq_act_bytes, fq_dequant_rows, fq_device_init, fq_fold_gain, fq_geglu,
                        fq_gemm, fq_gemm_heads, fq_test_hook,
-                       fq_linear, fq_linear_heads,
+                       fq_linear, fq_linear_heads, fq_linear_noalloc, fq_linear_noalloc_max_bytes,
                        fq_linear_workspace_bytes, fq_pack_weights, fq_prologue, fq_weight_bytes, last_error,
                        lib)
 from .site import DeviceSite
 
 __all__ = [
     "FqError", "abi_version", "fq_act_bytes", "fq_device_init", "fq_fold_gain", "fq_test_hook", "fq_geglu",
-    "fq_gemm", "fq_gemm_heads", "fq_linear", "fq_linear_heads", "fq_linear_workspace_bytes",
+    "fq_gemm", "fq_gemm_heads", "fq_linear", "fq_linear_heads", "fq_linear_noalloc", "fq_linear_noalloc_max_bytes",
+    "fq_linear_workspace_bytes",
     "fq_pack_weights", "fq_dequant_rows", "fq_prologue", "fq_weight_bytes", "last_error", "lib", "DeviceSite",
 ]

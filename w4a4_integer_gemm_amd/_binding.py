@@ -40,6 +40,9 @@ SIGNATURES = {
     "fq_linear_workspace_bytes": ([_I32, _I32, _I32], _SZ),
     "fq_linear": ([_P, _I32, _I32, _I64, _P, _F, _P, _I32, _I32, _I32, _P, _P, _I32, _I32, _P, _P, _I64, _P,
                    _I64, _P, _SZ, _P], ctypes.c_int),
+    "fq_linear_noalloc": ([_P, _I32, _I32, _I64, _P, _F, _P, _I32, _I32, _I32, _P, _P, _I32, _I32, _P, _P, _I64, _P,
+                           _I64, _P], ctypes.c_int),
+    "fq_linear_noalloc_max_bytes": ([], _SZ),
     "fq_linear_heads": ([_P, _I32, _I32, _I64, _P, _F, _P, _I32, _I32, _I32, _P, _P, _I32, _I32, _P, _P, _I64,
                          _I32, _P, _P, _SZ, _P], ctypes.c_int),
 }
@@ -180,6 +183,18 @@ def fq_linear(x, M: int, K: int, ldx: int, gamma_folded, eps: float, ascale, fol
     _check(lib().fq_linear(_dptr(x), M, K, ldx, _dptr(gamma_folded), eps, _dptr(ascale), fold_after, hblock, abits,
                            _dptr(w_codes), _dptr(wscale), N, wbits, _dptr(bias), _dptr(residual), ldr, _dptr(y),
                            ldy, _dptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def fq_linear_noalloc(x, M: int, K: int, ldx: int, gamma_folded, eps: float, ascale, fold_after: int, hblock: int,
+                      abits: int, w_codes, wscale, N: int, wbits: int, bias, residual, ldr: int, y, ldy: int,
+                      stream=None):
+    _check(lib().fq_linear_noalloc(_dptr(x), M, K, ldx, _dptr(gamma_folded), eps, _dptr(ascale), fold_after, hblock,
+                                   abits, _dptr(w_codes), _dptr(wscale), N, wbits, _dptr(bias), _dptr(residual), ldr,
+                                   _dptr(y), ldy, _stream(stream)))
+
+
+def fq_linear_noalloc_max_bytes() -> int:
+    return lib().fq_linear_noalloc_max_bytes()
 
 
 def fq_gemm_heads(act_codes, act_scale, M: int, abits: int, w_codes, wscale, N: int, K: int, wbits: int, bias,

@@ -88,6 +88,7 @@ hipError_t init_device(int dev, DeviceInfo& d) {
     if (e == hipSuccess) e = hipDeviceGetAttribute(&d.lds_per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev);
     if (e == hipSuccess && (d.cus < 1 || d.lds_per_cu < 1)) e = hipErrorInvalidDevice;
     if (e == hipSuccess) e = init_gemv_device(d);
+    if (e == hipSuccess) e = init_scratch_device(d);
     return e;
 }
 
@@ -169,10 +170,11 @@ fq_status check_hblock(const char* fn, int32_t K, int32_t hblock) {
 
 fq_status validate_prologue(const char* fn, const void* x, int32_t M, int32_t K, int64_t ldx,
                             const float* gamma, float eps, const float* ascale, int32_t fold_after,
-                            int32_t hblock, int32_t abits, const void* codes, const float* scale) {
+                            int32_t hblock, int32_t abits, const void* codes, const float* scale,
+                            bool check_out = true) {
     if (!x) return fail(FQ_ERR_ARG, fmt("%s: x_bf16 is NULL", fn));
-    if (!codes) return fail(FQ_ERR_ARG, fmt("%s: act_codes is NULL", fn));
-    if (!scale) return fail(FQ_ERR_ARG, fmt("%s: act_scale is NULL", fn));
+    if (check_out && !codes) return fail(FQ_ERR_ARG, fmt("%s: act_codes is NULL", fn));
+    if (check_out && !scale) return fail(FQ_ERR_ARG, fmt("%s: act_scale is NULL", fn));
     if (M < 1) return fail(FQ_ERR_SHAPE, fmt("%s: M=%d must be >= 1", fn, M));
     FQ_TRY(check_k(fn, K, kProloguePack));
     if (K > 32768 && K % 64)
@@ -187,8 +189,8 @@ fq_status validate_prologue(const char* fn, const void* x, int32_t M, int32_t K,
     if (gamma && !(eps >= 0.0f && eps < 1e30f))
         return fail(FQ_ERR_ARG, fmt("%s: eps=%g must be finite and >= 0", fn, (double)eps));
     if (!aligned(x, 16)) return fail(FQ_ERR_ALIGN, fmt("%s: x_bf16 is not 16-byte aligned", fn));
-    if (!aligned(codes, 16)) return fail(FQ_ERR_ALIGN, fmt("%s: act_codes is not 16-byte aligned", fn));
-    if (!aligned(scale, 4)) return fail(FQ_ERR_ALIGN, fmt("%s: act_scale is not 4-byte aligned", fn));
+    if (check_out && !aligned(codes, 16)) return fail(FQ_ERR_ALIGN, fmt("%s: act_codes is not 16-byte aligned", fn));
+    if (check_out && !aligned(scale, 4)) return fail(FQ_ERR_ALIGN, fmt("%s: act_scale is not 4-byte aligned", fn));
     if (gamma && !aligned(gamma, 16)) return fail(FQ_ERR_ALIGN, fmt("%s: gamma_folded is not 16-byte aligned", fn));
     if (ascale && !aligned(ascale, 16)) return fail(FQ_ERR_ALIGN, fmt("%s: ascale is not 16-byte aligned", fn));
     return FQ_OK;
@@ -334,32 +336,53 @@ fq_status gemm_impl(const char* fn, const void* act_codes, const float* act_scal
     return run_gemm(fn, g, *dev, static_cast<hipStream_t>(stream));
 }
 
+// fq_linear and its variants.  With use_scratch the workspace is this
+// device's scratch array (fq_linear_noalloc) and workspace/workspace_bytes
+// are ignored.
 fq_status linear_impl(const char* fn, const void* x_bf16, int32_t M, int32_t K, int64_t ldx,
                       const float* gamma_folded, float eps, const float* ascale, int32_t fold_after, int32_t hblock,
                       int32_t abits, const void* w_codes, const float* wscale, int32_t N, int32_t wbits,
                       const float* bias, const void* residual_bf16, int64_t ldr, void* y_bf16, int64_t ldy,
-                      int32_t head_dim, void* workspace, size_t workspace_bytes, void* stream) {
+                      int32_t head_dim, void* workspace, size_t workspace_bytes, void* stream,
+                      bool use_scratch = false) {
     fq::clear_error();
-    if (!workspace) return fail(FQ_ERR_ARG, fmt("%s: workspace is NULL", fn));
-    if (!aligned(workspace, 256)) return fail(FQ_ERR_ALIGN, fmt("%s: workspace is not 256-byte aligned", fn));
+    if (!use_scratch && !workspace) return fail(FQ_ERR_ARG, fmt("%s: workspace is NULL", fn));
+    if (!use_scratch && !aligned(workspace, 256))
+        return fail(FQ_ERR_ALIGN, fmt("%s: workspace is not 256-byte aligned", fn));
     // shape checks first so that the workspace size below is meaningful
     if (M < 1) return fail(FQ_ERR_SHAPE, fmt("%s: M=%d must be >= 1", fn, M));
     FQ_TRY(check_k(fn, K, kGemmK));
     FQ_TRY(check_bits(fn, "abits", abits));
     const size_t need = fq_linear_workspace_bytes(M, K, abits);
-    if (workspace_bytes < need)
+    if (use_scratch) {
+        if (need > fq::kNoallocScratchBytes)
+            return fail(FQ_ERR_UNSUPPORTED,
+                        fmt("%s: M=%d K=%d abits=%d needs %zu bytes of codes and scales, more than the %zu-byte "
+                            "scratch array; use fq_linear with a caller workspace",
+                            fn, M, K, abits, need, fq::kNoallocScratchBytes));
+    } else if (workspace_bytes < need) {
         return fail(FQ_ERR_ARG, fmt("%s: workspace_bytes=%zu < %zu needed for M=%d K=%d abits=%d", fn,
                                     workspace_bytes, need, M, K, abits));
+    }
+    // the device set-up (which also gives this device's scratch address) is
+    // the last host-side step that can fail; it runs before anything is queued
+    const fq::DeviceInfo* dev = nullptr;
+    if (use_scratch) {
+        // validate everything that does not depend on the workspace address first
+        FQ_TRY(validate_prologue(fn, x_bf16, M, K, ldx, gamma_folded, eps, ascale, fold_after, hblock, abits,
+                                 nullptr, nullptr, false));
+        FQ_TRY(validate_gemm(fn, nullptr, nullptr, M, abits, w_codes, wscale, N, K, wbits, bias, residual_bf16, ldr,
+                             y_bf16, ldy, false, head_dim));
+        FQ_TRY(prepare(fn, &dev));
+        workspace = dev->scratch;
+    }
     uint8_t* codes = static_cast<uint8_t*>(workspace);
     float* scales = reinterpret_cast<float*>(codes + round_up(code_bytes(M, K, abits), 256));
     FQ_TRY(validate_prologue(fn, x_bf16, M, K, ldx, gamma_folded, eps, ascale, fold_after, hblock, abits, codes,
                              scales));
     FQ_TRY(validate_gemm(fn, codes, scales, M, abits, w_codes, wscale, N, K, wbits, bias, residual_bf16, ldr,
                          y_bf16, ldy, true, head_dim));
-    // every host-side step that can fail (the device set-up) runs before the
-    // prologue is queued; after it only the GEMM's launch itself can fail
-    const fq::DeviceInfo* dev = nullptr;
-    FQ_TRY(prepare(fn, &dev));
+    if (!use_scratch) FQ_TRY(prepare(fn, &dev));
     hipStream_t s = static_cast<hipStream_t>(stream);
     fq::PrologueArgs a{static_cast<const uint16_t*>(x_bf16), M, K, ldx, gamma_folded, eps, ascale,
                        fold_after, hblock, abits, codes, scales};
@@ -423,6 +446,17 @@ fq_status fq_geglu(const void* gateup_bf16, int32_t M, int32_t F, int64_t ld_in,
                                               static_cast<uint16_t*>(h_bf16), ld_out,
                                               static_cast<hipStream_t>(stream)));
 }
+
+fq_status fq_linear_noalloc(const void* x_bf16, int32_t M, int32_t K, int64_t ldx, const float* gamma_folded,
+                            float eps, const float* ascale, int32_t fold_after, int32_t hblock, int32_t abits,
+                            const void* w_codes, const float* wscale, int32_t N, int32_t wbits, const float* bias,
+                            const void* residual_bf16, int64_t ldr, void* y_bf16, int64_t ldy, void* stream) {
+    return linear_impl("fq_linear_noalloc", x_bf16, M, K, ldx, gamma_folded, eps, ascale, fold_after, hblock, abits,
+                       w_codes, wscale, N, wbits, bias, residual_bf16, ldr, y_bf16, ldy, 0, nullptr, 0, stream,
+                       true);
+}
+
+size_t fq_linear_noalloc_max_bytes(void) { return fq::kNoallocScratchBytes; }
 
 fq_status fq_linear_heads(const void* x_bf16, int32_t M, int32_t K, int64_t ldx, const float* gamma_folded,
                           float eps, const float* ascale, int32_t fold_after, int32_t hblock, int32_t abits,

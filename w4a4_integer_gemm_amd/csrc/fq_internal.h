@@ -77,11 +77,18 @@ struct DeviceInfo {
     int cus;
     int lds_per_cu;
     int stream_regs_wg[4][2];  // [bit mix: 8/8, 4/4, 8/4, 4/8][token tiles - 1]
+    void* scratch;             // this device's copy of the allocation-free workspace
 };
+
+// Size of the device array that fq_linear_noalloc uses as its workspace (the
+// activation codes and scales, laid out as fq_linear's workspace).
+constexpr size_t kNoallocScratchBytes = size_t(24) << 20;
 // Set-up of the current device (once); *info points at its record.
 hipError_t prepare_device(const DeviceInfo** info);
 // The streaming GEMV's part of that set-up (fq_gemv.hip).
 hipError_t init_gemv_device(DeviceInfo& d);
+// The address of this device's scratch array (fq_noalloc.hip).
+hipError_t init_scratch_device(DeviceInfo& d);
 
 // Enqueue the kernels; they return hipGetLastError() of the launch.  Shapes
 // are validated by the caller; a launch makes no other HIP call.

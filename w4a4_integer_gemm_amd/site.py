@@ -99,6 +99,16 @@ class DeviceSite:
                     0 if residual is None else residual.stride(0), y, y.stride(0), ws, ws.numel(), stream)
         return y
 
+    def linear_noalloc(self, x, residual=None, y=None, stream=None):
+        """fq_linear_noalloc: as linear(), with the library's per-GPU scratch array as the workspace."""
+        M = x.shape[0]
+        if y is None:
+            y = self.empty_out(M)
+        B.fq_linear_noalloc(x, M, self.K, x.stride(0), self.gamma, self.eps, self.ascale, self.fold_after,
+                            self.hblock, self.abits, self.codes, self.wscale, self.N, self.wbits, self.bias, residual,
+                            0 if residual is None else residual.stride(0), y, y.stride(0), stream)
+        return y
+
     def linear_heads(self, x, head_dim: int, residual=None, y=None, stream=None):
         """fq_linear_heads: y is [N / head_dim][M][head_dim] (int16 tensor of bf16 bits)."""
         import torch
