@@ -395,20 +395,27 @@ def measure_ceilings(stream_bytes=135_790_592, copies=5):
     n16 = stream_bytes // 16
     bufs = [torch.randint(-128, 128, (stream_bytes,), dtype=torch.int8, device="cuda") for _ in range(copies)]
     best = (0.0, None)
-    for per_cu in (4, 8, 16):
-        for u in (4, 8, 16):
-            i = [0]
+    i = [0]
 
-            def run():
-                L.fqc_stream_read(bufs[i[0] % copies].data_ptr(), n16, cus * per_cu, u, out.data_ptr(), stream)
-                i[0] += 1
-            for _ in range(20):
-                run()
-            ms = _event_ms(run, 50)
-            gbs = n16 * 16 / (ms * 1e-3) / 1e9
-            res["stream_read"][f"{per_cu}wg_per_cu_u{u}"] = gbs
-            if gbs > best[0]:
-                best = (gbs, f"{cus * per_cu} workgroups of 256, {u} x 16-byte loads in flight per lane")
+    def reader(per_cu, u):
+        def run():
+            L.fqc_stream_read(bufs[i[0] % copies].data_ptr(), n16, cus * per_cu, u, out.data_ptr(), stream)
+            i[0] += 1
+        return run
+    warm_up(reader(8, 4), 20)  # the memory system under load before the sweep
+    # two passes over the launch shapes, 100 launches (about 2 ms) each; the best pass counts
+    for _ in range(2):
+        for per_cu in (4, 8, 16):
+            for u in (4, 8, 16):
+                run = reader(per_cu, u)
+                for _ in range(10):
+                    run()
+                ms = _event_ms(run, 100)
+                gbs = n16 * 16 / (ms * 1e-3) / 1e9
+                key = f"{per_cu}wg_per_cu_u{u}"
+                res["stream_read"][key] = max(gbs, res["stream_read"].get(key, 0.0))
+                if gbs > best[0]:
+                    best = (gbs, f"{cus * per_cu} workgroups of 256, {u} x 16-byte loads in flight per lane")
     res["stream_read_gbs"] = best[0]
     res["stream_read_config"] = best[1]
     res["stream_read_buffers"] = f"{copies} rotated buffers of {stream_bytes} bytes"
