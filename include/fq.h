@@ -101,6 +101,7 @@ fq_status fq_device_init(void);
  *   gemm_tile=<128x128|128x144|128x112|128x96|64x128|64x224|64x256|64x288|64x128x2|auto>
  *   gemm_mfma=<16|32>     (8-bit x 8-bit codes on v_mfma_i32_32x32x32_i8 with 32)
  *   gemv=<split|auto>     (decode-sized M always on the split-K GEMV kernel)
+ *   decode1=<off|auto>    (one-token fq_linear as two launches, not the fused kernel)
  * The environment variable FQ_TEST_HOOK, read once per process at the hooks'
  * first use, takes the same spec.  FQ_ERR_ARG on an unknown key or value (state kept).
  * Process-wide; a call while another thread launches races with it. */
@@ -186,7 +187,10 @@ size_t fq_linear_workspace_bytes(int32_t M, int32_t K, int32_t abits);
 
 /* Prologue then GEMM on one stream; arguments as in fq_prologue and fq_gemm.
  * workspace: device, at least fq_linear_workspace_bytes(M, K, abits) bytes,
- * 256-byte aligned; it holds the codes and scales after the call. */
+ * 256-byte aligned; it holds the codes and scales after the call.  A single
+ * token (M = 1, K <= 4096, hblock 32, 64 or 128) runs as one launch in which
+ * every workgroup quantises the token while its weight loads are in flight;
+ * codes, scale and outputs are those of the two launches, bit for bit. */
 fq_status fq_linear(const void* x_bf16, int32_t M, int32_t K, int64_t ldx,
                     const float* gamma_folded, float eps, const float* ascale,
                     int32_t fold_after, int32_t hblock, int32_t abits,

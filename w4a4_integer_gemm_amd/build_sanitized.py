@@ -26,7 +26,7 @@ LIB = os.path.join(HERE, "libfq_san.so")
 ORACLE_LIB = os.path.join(ROOT, "oracle", "liboracle_san.so")
 SAN = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g"]
 HOST_SOURCES = ["fq_api.cpp", "fq_pack.cpp"]
-DEVICE_OBJECTS = ["fq_prologue.o", "fq_gemm.o", "fq_gemv.o", "fq_geglu.o", "fq_noalloc.o"]
+DEVICE_OBJECTS = ["fq_prologue.o", "fq_gemm.o", "fq_gemv.o", "fq_geglu.o", "fq_noalloc.o", "fq_decode1.o"]
 TESTS = ["tests/test_abi_cpu.py", "tests/test_oracle_pins.py", "tests/test_fold_consistency.py"]
 
 

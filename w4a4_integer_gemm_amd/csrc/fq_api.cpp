@@ -26,10 +26,10 @@ void clear_error() { g_error.clear(); }
 namespace {
 
 // Applies a test-hook spec "key=value,key=value" (keys gemm_tile, gemm_mfma,
-// gemv; "" or "default" resets every hook).  Returns false, with the reason in
+// gemv, decode1; "" or "default" resets every hook).  Returns false, with the reason in
 // *why, on an unknown key or value; nothing changes then.
 bool apply_hooks(Hooks& h, const char* spec, std::string* why) {
-    int tile = -1, mfma = 16, split = 0;
+    int tile = -1, mfma = 16, split = 0, d1off = 0;
     std::string s = spec ? spec : "";
     if (s == "default") s.clear();
     size_t pos = 0;
@@ -59,14 +59,21 @@ bool apply_hooks(Hooks& h, const char* spec, std::string* why) {
                 return false;
             }
             split = val == "split";
+        } else if (key == "decode1") {
+            if (val != "off" && val != "auto") {
+                *why = "decode1 must be off or auto, not '" + val + "'";
+                return false;
+            }
+            d1off = val == "off";
         } else {
-            *why = "unknown hook '" + key + "' (gemm_tile, gemm_mfma, gemv)";
+            *why = "unknown hook '" + key + "' (gemm_tile, gemm_mfma, gemv, decode1)";
             return false;
         }
     }
     h.gemm_tile.store(tile, std::memory_order_relaxed);
     h.gemm_mfma.store(mfma, std::memory_order_relaxed);
     h.gemv_split.store(split, std::memory_order_relaxed);
+    h.decode1_off.store(d1off, std::memory_order_relaxed);
     return true;
 }
 
@@ -386,10 +393,12 @@ fq_status linear_impl(const char* fn, const void* x_bf16, int32_t M, int32_t K, 
     hipStream_t s = static_cast<hipStream_t>(stream);
     fq::PrologueArgs a{static_cast<const uint16_t*>(x_bf16), M, K, ldx, gamma_folded, eps, ascale,
                        fold_after, hblock, abits, codes, scales};
-    FQ_TRY(device_status(fn, fq::launch_prologue(a, s)));
     fq::GemmArgs g{codes, scales, M, abits, static_cast<const uint8_t*>(w_codes), wscale, N, K, wbits, bias,
                    static_cast<const uint16_t*>(residual_bf16), ldr, static_cast<uint16_t*>(y_bf16), ldy,
                    nullptr, head_dim};
+    // one token: prologue and GEMV in one launch (the same codes, scale and outputs)
+    if (fq::decode1_eligible(a, g)) return device_status(fn, fq::launch_decode1(a, g, s));
+    FQ_TRY(device_status(fn, fq::launch_prologue(a, s)));
     return run_gemm(fn, g, *dev, s);
 }
 

@@ -17,64 +17,13 @@
 #include <hip/hip_runtime.h>
 
 #include "fq_device.h"
+#include "fq_gemv_unit.h"
 #include "fq_internal.h"
 
 namespace fq {
 namespace {
 
 constexpr int kMaxWaves = 8;
-
-// k per unit and the bytes of one lane's activation codes per unit.
-template <int ABITS, int WBITS>
-struct Unit {
-    static constexpr int K = WBITS == 8 ? 64 : 128;
-    static constexpr int WROW = K * WBITS / 8;       // weight bytes per row per unit (64)
-    static constexpr int AROW = K * ABITS / 8;       // activation bytes per token per unit
-    static constexpr int ALANE = AROW / 4;           // 8, 16 or 32
-    static constexpr int AREGS = ALANE > 16 ? 2 : 1; // 16-byte registers per lane
-};
-
-// One lane's activation codes of one unit (8, 16 or 32 bytes).
-struct ActReg {
-    uint4 v[2];
-};
-
-template <int ABITS, int WBITS>
-__device__ __forceinline__ void load_act(ActReg& a, const uint8_t* p, bool ok) {
-    using U = Unit<ABITS, WBITS>;
-    a.v[0] = make_uint4(0, 0, 0, 0);
-    a.v[1] = make_uint4(0, 0, 0, 0);
-    if (ok) {
-        if (U::ALANE == 8) {
-            const uint2 t = *reinterpret_cast<const uint2*>(p);
-            a.v[0] = make_uint4(t.x, t.y, 0, 0);
-        } else {
-            a.v[0] = *reinterpret_cast<const uint4*>(p);
-            if (U::AREGS == 2) a.v[1] = *reinterpret_cast<const uint4*>(p + 16);
-        }
-    }
-}
-
-// acc += the unit's product; w = the lane's 16 weight bytes.
-//  8-bit weights: one MFMA over k = 16 q + [0, 16) of the unit.
-//  4-bit weights: the lane's 32 nibbles are k = 32 q + [0, 32); MFMA j takes
-//  bytes 8 j .. 8 j + 7 of both operands, k = 32 q + 16 j + [0, 16).
-template <int ABITS, int WBITS>
-__device__ __forceinline__ v4i unit_mfma(const uint4 w, const ActReg& a, v4i acc) {
-    if (WBITS == 8) {
-        if (ABITS == 8) return mfma16x16x64(frag_from_bytes(w), frag_from_bytes(a.v[0]), acc);
-        return mfma16x16x64(frag_from_bytes_nibble_order(w), frag_from_nibbles(make_uint2(a.v[0].x, a.v[0].y)),
-                            acc);
-    }
-    const v4i w0 = frag_from_nibbles(make_uint2(w.x, w.y));
-    const v4i w1 = frag_from_nibbles(make_uint2(w.z, w.w));
-    if (ABITS == 4) {
-        acc = mfma16x16x64(w0, frag_from_nibbles(make_uint2(a.v[0].x, a.v[0].y)), acc);
-        return mfma16x16x64(w1, frag_from_nibbles(make_uint2(a.v[0].z, a.v[0].w)), acc);
-    }
-    acc = mfma16x16x64(w0, frag_from_bytes_nibble_order(a.v[0]), acc);
-    return mfma16x16x64(w1, frag_from_bytes_nibble_order(a.v[1]), acc);
-}
 
 // grid: one workgroup per R groups of 16 rows; block: S waves; `per` units per wave.
 // Each wave loads a unit's activation codes once and uses them for its R row
@@ -237,18 +186,6 @@ __host__ __device__ inline size_t stream_lds_bytes(int mt, int pitch) {
     return size_t(16 * mt) * size_t(pitch) + size_t(2 * kLoadWaves * mt) * 64 * 16 + 128;
 }
 
-template <int ABITS, int WBITS>
-__device__ __forceinline__ void lds_act(ActReg& a, const uint8_t* p) {
-    using U = Unit<ABITS, WBITS>;
-    a.v[1] = make_uint4(0, 0, 0, 0);
-    if (U::ALANE == 8) {
-        const uint2 t = *reinterpret_cast<const uint2*>(p);
-        a.v[0] = make_uint4(t.x, t.y, 0, 0);
-    } else {
-        a.v[0] = *reinterpret_cast<const uint4*>(p);
-        if (U::AREGS == 2) a.v[1] = *reinterpret_cast<const uint4*>(p + 16);
-    }
-}
 
 // grid: resident workgroups, each taking every gridDim-th of the `groups`
 // 16-row groups; block: 8 waves (at most 128 VGPRs: two workgroups per CU

@@ -60,6 +60,7 @@ struct Hooks {
     std::atomic<int> gemm_tile{-1};  // -1: the cost model picks; else a tile id of fq_gemm.hip
     std::atomic<int> gemm_mfma{16};  // 16: v_mfma_i32_16x16x64_i8 where it applies; 32: 32x32x32 only
     std::atomic<int> gemv_split{0};  // 1: decode-sized M always takes the split-K GEMV
+    std::atomic<int> decode1_off{0}; // 1: one-token fq_linear as two launches, never the fused kernel
 };
 Hooks& hooks();
 // Tile id of a tile name ("128x144", ...), or -1 (fq_gemm.hip).
@@ -95,6 +96,10 @@ hipError_t init_scratch_device(DeviceInfo& d);
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t stream);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_gemv(const GemmArgs& a, const DeviceInfo& dev, hipStream_t stream);
+// One-token fq_linear in one launch (fq_decode1.hip): whether the shape takes
+// it, and the launch (prologue arguments and GEMM arguments of the same call).
+bool decode1_eligible(const PrologueArgs& p, const GemmArgs& g);
+hipError_t launch_decode1(const PrologueArgs& p, const GemmArgs& g, hipStream_t stream);
 hipError_t launch_geglu(const uint16_t* gu, int32_t M, int32_t F, int64_t ld_in, uint16_t* h, int64_t ld_out,
                         hipStream_t stream);
 

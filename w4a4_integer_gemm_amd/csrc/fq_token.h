@@ -226,6 +226,24 @@ __device__ __forceinline__ TokenLoad<E, NORM> load_token(const uint16_t* __restr
     return t;
 }
 
+// The same loads with no condition: lanes past K load lane 0's values, which
+// quantise_loaded leaves out of its sums and maxima.  With every load
+// unconditional the compiler's memory-counter waits stay exact, so a caller
+// that issues other loads after these waits only for these.
+template <int E, bool NORM>
+__device__ __forceinline__ TokenLoad<E, NORM> load_token_clamped(const uint16_t* __restrict__ xr, int K,
+                                                                 const float* __restrict__ gamma, int c) {
+    TokenLoad<E, NORM> t;
+    const int cc = c < K / E ? c : 0;
+#pragma unroll
+    for (int q = 0; q < E / 8; ++q) t.d[q] = *reinterpret_cast<const uint4*>(xr + E * cc + 8 * q);
+    if constexpr (TokenLoad<E, NORM>::kPreG) {
+#pragma unroll
+        for (int q = 0; q < E / 4; ++q) t.g[q] = *reinterpret_cast<const float4*>(gamma + E * cc + 4 * q);
+    }
+    return t;
+}
+
 // Quantise one loaded token: RMSNorm with the folded gain (NORM), the optional
 // smoothing divide (AMODE 0 none, 1 before the rotation, 2 after it), the
 // block Hadamard rotation of 2^LOG2B values and the per-token symmetric
@@ -244,7 +262,7 @@ __device__ __forceinline__ float quantise_loaded(const TokenLoad<E, NORM>& t, in
     constexpr int qmax = ABITS == 8 ? 127 : 7;
     const int lane = c & 63;
     const int wave = c >> 6;
-    const bool active = c < K / E;  // lanes past K hold zeros and only join the exchanges
+    const bool active = c < K / E;  // lanes past K only join the exchanges; their values are left out
 
     constexpr bool kPreG = TokenLoad<E, NORM>::kPreG;
     float v[E];
@@ -254,7 +272,7 @@ __device__ __forceinline__ float quantise_loaded(const TokenLoad<E, NORM>& t, in
 
     // RMSNorm with the folded gain: the float32 squares are exact in float64
     if (NORM) {
-        double ss = wave_sum(lane_sumsq<E>(v));
+        double ss = wave_sum(active ? lane_sumsq<E>(v) : 0.0);
         if (nwaves > 1) {
             if (lane == 0) red_d[wave] = ss;
             __syncthreads();
@@ -305,7 +323,7 @@ __device__ __forceinline__ float quantise_loaded(const TokenLoad<E, NORM>& t, in
     if (AMODE == 2) divide_by_vector<E>(v, ascale, c, active);
 
     // per-token amax (lanes past K hold zeros)
-    float amax = wave_max(lane_absmax<E>(v));
+    float amax = wave_max(active ? lane_absmax<E>(v) : 0.0f);
     if (nwaves > 1) {
         if (lane == 0) red_f[wave] = amax;
         __syncthreads();
