@@ -184,6 +184,44 @@ def parity(wl, site, y, codes, scales, nrows=8):
     return ok, dict(rows_checked=len(rows), code_mismatch_frac=mism, code_max_diff=maxd, y_rel_fro=fro)
 
 
+def bench_mlp_block(steps, warmup):
+    """The Gemma-shaped W4A4 MLP block chained on the GPU: gate+up site (816 x
+    2048 -> 32768) -> GeGLU -> down site (16384 -> 2048) with the residual, the
+    down site reading the GeGLU output of the gate+up site.  TOPS over the two
+    GEMMs' 2*M*N*K; the parity control recomputes sampled tokens of each node
+    with the oracle from that node's own GPU inputs."""
+    import torch
+    import synth
+    import w4a4_integer_gemm_amd as fq
+    up = synth.make_workload("gateup_w4a4")
+    F = up.N // 2
+    dn = synth.make_workload("down_w4a4")
+    s_up, s_dn = site_for(up), site_for(dn)
+    x = s_up.upload(up.x)
+    y1 = s_up.empty_out(up.M)
+    h = torch.empty((up.M, F), dtype=torch.int16, device="cuda")
+    y2 = s_dn.empty_out(up.M)
+    s_up.workspace(up.M)
+    s_dn.workspace(up.M)
+
+    def step():
+        s_up.linear(x, y=y1)
+        fq.fq_geglu(y1, up.M, F, 2 * F, h, F)
+        s_dn.linear(h, residual=x, y=y2)
+    nwarm = warm_up(step, warmup)
+    ms, batches = timed_steps(step, steps)
+    ms_graph, _ = graph_steps(step, steps)
+    step()
+    torch.cuda.synchronize()
+    # parity of the down node from its own GPU input h
+    dn.x = h.cpu().numpy().view(np.uint16)
+    dn.residual = up.x
+    ok, detail = parity(dn, s_dn, y2, *s_dn.workspace_codes(up.M))
+    ops = 2.0 * up.M * (up.N * up.K + dn.N * dn.K)
+    return dict(ms=ms, tops=ops / (ms * 1e-3) / 1e12, ms_graph=ms_graph, tops_graph=ops / (ms_graph * 1e-3) / 1e12,
+                batches=batches, parity=detail, parity_ok=ok, warmup_run=nwarm)
+
+
 def bench_decode(name, steps, warmup, copies=5):
     """Decode GEMV GB/s with the weights rotated over `copies` device copies
     (5 x 136 MB > 2 x the 256 MB Infinity Cache) so each call streams from HBM."""
@@ -556,6 +594,15 @@ def main():
                               "ms_prologue": s["ms_prologue"], "ms_gemm": s["ms_gemm"], "parity": s["parity"]})
             del s
             torch.cuda.empty_cache()
+        m = bench_mlp_block(max(20, args.steps // 4), args.warmup)
+        secondary.append({"workload": "gemma_mlp_block_w4a4", "metric": "MLP block TOPS (two GEMMs)",
+                          "value": m["tops"], "frac_int8_peak": m["tops"] / PEAK_INT8_TOPS, "ms_per_call": m["ms"],
+                          "graph": {"value": m["tops_graph"], "ms_per_call": m["ms_graph"]},
+                          "batch_spread": m["batches"], "parity_down_node": m["parity"],
+                          "chain": "gate+up fq_linear (816x2048->32768) -> fq_geglu -> down fq_linear "
+                                   "(16384->2048, residual = the block input)"})
+        del m
+        torch.cuda.empty_cache()
         # the tiny 16-token site: latency only
         s = bench_prefill("tiny_w8a8", max(50, args.steps), args.warmup)
         secondary.append({"workload": "tiny_w8a8", "metric": "fq_linear latency", "value": s["ms"] * 1e3,

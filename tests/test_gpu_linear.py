@@ -8,7 +8,7 @@ import pytest
 import oracle
 import synth
 import w4a4_integer_gemm_amd as fq
-from fqtest import assert_codes, assert_y_elementwise, assert_y_fro, dev, host, log
+from fqtest import assert_codes, assert_y_elementwise, assert_y_fro, assert_y_within, dev, host, log
 
 pytestmark = pytest.mark.gpu
 
@@ -89,24 +89,42 @@ def test_linear_workload_full_size_sampled(name):
 
 @pytest.mark.parametrize("name,max_rel", [("qkv_w8a8", 0.03), ("gateup_w4a4", 0.35)])
 def test_dequant_float_path_agrees_with_integer_path(name, max_rel):
-    """The page's dequant mode: a float GEMM on the un-rotated activations with the
-    rows fq_dequant_rows rebuilds (the smoothing vector stays in the folded norm
-    gain) computes the same layer as the integer path, up to the activations'
-    quantisation (8-bit: ~1 %, 4-bit: 15 levels)."""
+    """The page's dequant mode: a float GEMM with the rows fq_dequant_rows
+    rebuilds (the smoothing vector stays in the folded norm gain).
+
+    Exact check: the GPU's own activation codes, dequantised and rotated back
+    to the original frame (x_deq = R(s_a q_a); R is its own inverse), times
+    the dequantised rows give the integer path's result up to float64
+    rounding, because R(s_a q_a) . R(s_w q_w) = (s_a q_a) . (s_w q_w): every
+    GPU output must be that value rounded to bf16 (half a bf16 ulp plus the
+    epilogue's float32 rounding).  Informational: the float layer on the
+    unquantised activations differs by the activations' quantisation only
+    (8-bit: ~1 %, 4-bit: 15 levels), reported and bounded by max_rel."""
     wl = synth.make_workload(name, M=64, N=512)
     site = site_for(wl)
     y = host(site.linear(dev(wl.x)), np.uint16)
+    codes_d, scales_d = site.workspace_codes(wl.M)
+    qa = oracle.unpack_codes(host(codes_d).reshape(wl.M, -1), wl.K, wl.abits).astype(np.float64)
+    sa = host(scales_d).astype(np.float64)
+    W_deq = fq.fq_dequant_rows(site.codes_host, site.wscale_host, wl.K, None, 0, wl.hblock, wl.wbits)
+    x_deq = np.stack([oracle.rotate_f64(sa[m] * qa[m], wl.hblock) for m in range(wl.M)])
+    y_exact = x_deq @ W_deq.astype(np.float64).T
+    acc = (qa @ oracle.unpack_codes(site.codes_host, wl.K, wl.wbits).astype(np.float64).T)
+    # bound: the epilogue's float32 rounding of acc s_a s_w, plus the float32
+    # rounding of the dequantised rows (2^-24 of sum |x_deq| |W_deq|, written
+    # as a quarter of that sum on the 2^-21 scale of assert_y_within)
+    w_round = (np.abs(x_deq) @ np.abs(W_deq.astype(np.float64)).T) * 0.25
+    assert_y_within(y, y_exact, np.abs(acc * sa[:, None] * site.wscale_host.astype(np.float64)[None, :]) + w_round,
+                    what=f"{name} dequant rows x dequantised codes")
     y_int = synth.bf16_bits_to_f32(y).astype(np.float64)
     gamma_f = oracle.fold_gain(wl.gamma, wl.ascale).astype(np.float64)
     x = synth.bf16_bits_to_f32(wl.x).astype(np.float64)
     xn = x / np.sqrt(np.mean(x * x, axis=1, keepdims=True) + wl.eps) * gamma_f
-    W_deq = fq.fq_dequant_rows(site.codes_host, site.wscale_host, wl.K, None, 0, wl.hblock, wl.wbits)
     y_float = xn @ W_deq.astype(np.float64).T
     rel = np.linalg.norm(y_int - y_float) / np.linalg.norm(y_float)
     cos = float(np.sum(y_int * y_float) / (np.linalg.norm(y_int) * np.linalg.norm(y_float)))
-    log(f"dequant vs integer {name}: rel {rel:.3e} cosine {cos:.6f}")
+    log(f"dequant vs integer {name}: rel {rel:.3e} cosine {cos:.6f} (unquantised activations, informational)")
     assert rel <= max_rel and cos >= 1 - max_rel ** 2
-
 
 
 def test_decode_with_changing_token_counts():

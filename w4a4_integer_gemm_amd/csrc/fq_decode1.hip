@@ -12,16 +12,16 @@
 // what the two-launch path would have written.  The workgroup then runs the
 // split-K GEMV on R = 2 groups of 16 weight rows: 8 waves split K, each with
 // its units of both row groups in registers (PER units per wave, the last
-// unit repeated where K leaves fewer), the partial tiles meet in LDS and two
-// waves run the shared epilogue.
+// unit requested again where its share is smaller), the partial tiles meet in
+// LDS and two waves run the shared epilogue.
 //
 // The token is redone by every workgroup: N / 32 times in all, about 2.3 us
 // of VALU per SIMD at the 37888-row decode layer, spread over a launch that
 // streams 136 MB and leaves the VALU otherwise idle.  Measured (M = 1, K =
-// 3584, N = 37888, W8A8, weights rotated over 5 copies): 26.4 us against
-// 28.5 us for the prologue and the split-K GEMV as two launches; one row group
-// per workgroup 26.8 us, four 32.0 us (the register file then holds fewer
-// workgroups).
+// 3584, N = 37888, W8A8, weights rotated over 5 copies, one box): 27.0 us
+// against 28.3 us for the prologue and the split-K GEMV as two launches; one
+// row group per workgroup 27.5 us, three 29.3 us, four 32.7 us (the register
+// file then holds fewer workgroups).
 //
 // Taken when M = 1, K <= 4096 (8 values per lane over 512 lanes) and the
 // Hadamard block is 32, 64 or 128 (a block spans at most 16 lanes); other
@@ -128,10 +128,21 @@ template <int ABITS, int WBITS, bool NORM, int AMODE, int LOG2B>
 hipError_t launch_per(const PrologueArgs& p, const GemmArgs& g, int per, hipStream_t st) {
     const float rs = float(1.0 / std::sqrt(double(p.hblock)));
     const dim3 grid((g.N + 16 * kRows - 1) / (16 * kRows)), block(64 * kWaves);
-    if (per <= 4)
+    // PER: units per wave in registers, rounded up to 4 or 8, with 7 exact for
+    // 8-bit codes (the 3584-wide layers: 56 units over 8 waves; one unit
+    // repeated there measured 27.3 against 27.0 us)
+    if (per <= 4) {
         hipLaunchKernelGGL((decode1_kernel<ABITS, WBITS, NORM, AMODE, LOG2B, 4>), grid, block, 0, st, p, g, rs);
-    else
-        hipLaunchKernelGGL((decode1_kernel<ABITS, WBITS, NORM, AMODE, LOG2B, 8>), grid, block, 0, st, p, g, rs);
+        return hipGetLastError();
+    }
+    if constexpr (ABITS == 8 && WBITS == 8) {
+        if (per == 7) {
+            hipLaunchKernelGGL((decode1_kernel<ABITS, WBITS, NORM, AMODE, LOG2B, 7>), grid, block, 0, st, p, g,
+                               rs);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((decode1_kernel<ABITS, WBITS, NORM, AMODE, LOG2B, 8>), grid, block, 0, st, p, g, rs);
     return hipGetLastError();
 }
 
