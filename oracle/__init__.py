@@ -10,6 +10,15 @@ Every function below cites the passage of the vla.cpp pull request page
 it follows (section named in the docstring), and documents the reading taken
 where that page leaves a step open.
 
+Code width 6 (``E2M3``) is a storage form of the 4-bit codes, not a third
+quantiser: the same integers in [-7, 7] (qmax 7), each kept as a 6-bit OCP FP6
+E2M3 number (sign bit 5, two exponent bits with bias 1, three mantissa bits;
+exponent 0 is subnormal), which represents every one of them exactly.  Value k
+of a row sits in bits 6k .. 6k+5 of the row's bytes read as one little-endian
+bit string (3K/4 bytes per row).  Here it is a conversion wrapped around the
+4-bit functions: quantise with 4 bits, then re-store (``pack_e2m3``), and read
+back (``unpack_codes``) before the integer contraction.
+
 Pins: every function here is checked by ``tests/test_oracle_pins.py`` against
 closed forms, library routines (scipy's Sylvester Hadamard, numpy matmul and
 round-half-even, torch's bfloat16 cast), invariants and brute force.  The
@@ -30,7 +39,10 @@ __all__ = [
     "lib", "hadamard_entry", "rotate_f64", "butterfly_f32", "fold_gain", "fold_weights",
     "pack_weights", "unfold_weights", "act_frame", "prologue", "gemm_i32", "epilogue",
     "bf16_from_f64", "code_at", "num_threads", "unpack_codes", "linear", "row_bytes", "qmax", "geglu",
+    "E2M3", "e2m3_value", "e2m3_code", "pack_e2m3", "storage_bits",
 ]
+
+E2M3 = 6  # code width argument: 4-bit codes stored as FP6 E2M3
 
 _lib = None
 
@@ -83,12 +95,82 @@ def _check(rc: int, what: str):
 
 def qmax(bits: int) -> int:
     """Symmetric code range: +-127 for 8 bits, +-7 for 4 bits ("15 activation levels",
-    OpenVINO commit)."""
-    return {8: 127, 4: 7}[bits]
+    OpenVINO commit); the E2M3 storage holds the 4-bit codes."""
+    return {8: 127, 4: 7, E2M3: 7}[bits]
+
+
+def storage_bits(bits: int) -> int:
+    """The quantiser width behind a code width argument (E2M3 stores 4-bit codes)."""
+    return 4 if bits == E2M3 else bits
 
 
 def row_bytes(K: int, bits: int) -> int:
-    return K if bits == 8 else K // 2
+    return {8: K, 4: K // 2, E2M3: 3 * K // 4}[bits]
+
+
+def e2m3_value(code: int) -> float:
+    """The number a 6-bit FP6 E2M3 code stands for (OCP Microscaling formats
+    specification, FP6 E2M3: exponent bias 1, no infinities or NaN): sign bit 5,
+    exponent e = bits 4..3, mantissa m = bits 2..0; e = 0 gives m/8, otherwise
+    2^(e-1) (1 + m/8)."""
+    if not 0 <= code < 64:
+        raise ValueError(f"e2m3_value: {code} is not a 6-bit code")
+    sign = -1.0 if code & 32 else 1.0
+    e, m = (code >> 3) & 3, code & 7
+    mag = m / 8.0 if e == 0 else 2.0 ** (e - 1) * (1.0 + m / 8.0)
+    return sign * mag
+
+
+def e2m3_code(v: int) -> int:
+    """The E2M3 code of an integer code v in [-7, 7]: the 6-bit pattern whose value
+    is v (+0 for zero), found by search over the 64 patterns."""
+    if not -7 <= v <= 7:
+        raise ValueError(f"e2m3_code: {v} is outside [-7, 7]")
+    if v == 0:
+        return 0
+    for c in range(64):
+        if e2m3_value(c) == float(v):
+            return c
+    raise AssertionError("unreachable: every integer in [-7, 7] is an E2M3 number")
+
+
+_E2M3_OF = None  # code of v + 7, v in [-7, 7]
+_VAL_OF = None   # integer value of each 6-bit pattern (or 99 where it is no integer code)
+
+
+def _tables():
+    global _E2M3_OF, _VAL_OF
+    if _E2M3_OF is None:
+        _E2M3_OF = np.array([e2m3_code(v) for v in range(-7, 8)], np.uint32)
+        vals = [e2m3_value(c) for c in range(64)]
+        _VAL_OF = np.array([int(x) if x == int(x) and abs(x) <= 7 else 99 for x in vals], np.int32)
+    return _E2M3_OF, _VAL_OF
+
+
+def pack_e2m3(ints: np.ndarray) -> np.ndarray:
+    """Rows of integer codes in [-7, 7] -> E2M3 rows: value k in bits 6k .. 6k+5 of the
+    row's little-endian bit string (four values = three bytes)."""
+    q = np.asarray(ints)
+    if q.ndim != 2 or q.shape[1] % 4:
+        raise ValueError("pack_e2m3: rows of a multiple of 4 codes")
+    if q.size and (q.min() < -7 or q.max() > 7):
+        raise ValueError("pack_e2m3: codes outside [-7, 7]")
+    enc, _ = _tables()
+    c = enc[q.astype(np.int64) + 7].reshape(q.shape[0], q.shape[1] // 4, 4)
+    word = c[..., 0] | (c[..., 1] << 6) | (c[..., 2] << 12) | (c[..., 3] << 18)
+    out = np.empty((q.shape[0], q.shape[1] // 4, 3), np.uint8)
+    out[..., 0] = word & 0xFF
+    out[..., 1] = (word >> 8) & 0xFF
+    out[..., 2] = (word >> 16) & 0xFF
+    return out.reshape(q.shape[0], 3 * q.shape[1] // 4)
+
+
+def _to_nibbles(codes, K: int) -> np.ndarray:
+    """E2M3 rows -> the packed 4-bit rows of the same integers."""
+    q = unpack_codes(codes, K, E2M3)
+    lo = (q[:, 0::2] & 0xF).astype(np.uint8)
+    hi = (q[:, 1::2] & 0xF).astype(np.uint8)
+    return lo | (hi << 4)
 
 
 def hadamard_entry(b: int, i: int, j: int) -> int:
@@ -137,15 +219,20 @@ def pack_weights(W, ascale, fold_after: int, hblock: int, wbits: int):
     W = _c(W, np.float32)
     a = _c(ascale, np.float32)
     N, K = W.shape
-    codes = np.zeros((N, row_bytes(K, wbits)), np.uint8)
+    qb = storage_bits(wbits)
+    codes = np.zeros((N, row_bytes(K, qb)), np.uint8)
     ws = np.empty(N, np.float32)
-    _check(lib().fqo_pack_weights(_p(W), N, K, _p(a), fold_after, hblock, wbits, _p(codes), _p(ws)),
+    _check(lib().fqo_pack_weights(_p(W), N, K, _p(a), fold_after, hblock, qb, _p(codes), _p(ws)),
            "pack_weights")
+    if wbits == E2M3:
+        codes = pack_e2m3(unpack_codes(codes, K, 4))
     return codes, ws
 
 
 def unfold_weights(codes, wscale, K: int, ascale, fold_after: int, hblock: int, wbits: int):
     """Dequantised rows in the original frame: R(s q)/a or R(s q / a) (dequant-mode commit)."""
+    if wbits == E2M3:
+        codes, wbits = _to_nibbles(codes, K), 4
     codes = _c(codes, np.uint8)
     ws = _c(wscale, np.float32)
     a = _c(ascale, np.float32)
@@ -170,17 +257,25 @@ def prologue(x_bits, gamma, eps: float, ascale, fold_after: int, hblock: int, ab
     """Codes and per-token scales: amax scale, round-half-even, clamp (OpenVINO commit)."""
     x = _c(x_bits, np.uint16)
     M, K = x.shape
-    codes = np.zeros((M, row_bytes(K, abits)), np.uint8)
+    qb = storage_bits(abits)
+    codes = np.zeros((M, row_bytes(K, qb)), np.uint8)
     sc = np.empty(M, np.float32)
     _check(lib().fqo_prologue(_p(x), M, K, K, _p(_c(gamma, np.float32)), eps,
-                              _p(_c(ascale, np.float32)), fold_after, hblock, abits, _p(codes),
+                              _p(_c(ascale, np.float32)), fold_after, hblock, qb, _p(codes),
                               _p(sc)), "prologue")
+    if abits == E2M3:
+        codes = pack_e2m3(unpack_codes(codes, K, 4))
     return codes, sc
 
 
 def gemm_i32(act_codes, abits: int, w_codes, wbits: int, K: int) -> np.ndarray:
     """Exact integer contraction of the codes (runtime summary: integer GEMMs;
-    SYCL commit: integer sums are exact in any order)."""
+    SYCL commit: integer sums are exact in any order).  E2M3 rows are read back to
+    their integers first."""
+    if abits == E2M3:
+        act_codes, abits = _to_nibbles(act_codes, K), 4
+    if wbits == E2M3:
+        w_codes, wbits = _to_nibbles(w_codes, K), 4
     A = _c(act_codes, np.uint8)
     B = _c(w_codes, np.uint8)
     M, N = A.shape[0], B.shape[0]
@@ -228,13 +323,26 @@ def num_threads() -> int:
 
 
 def code_at(row: np.ndarray, k: int, bits: int) -> int:
+    if bits == E2M3:
+        return int(unpack_codes(np.asarray(row, np.uint8).reshape(1, -1), 4 * len(row) // 3, E2M3)[0, k])
     r = _c(row, np.uint8)
     return int(lib().fqo_code_at(_p(r), k, bits))
 
 
 def unpack_codes(codes: np.ndarray, K: int, bits: int) -> np.ndarray:
-    """Integer codes [rows][K] from int8 or packed 4-bit storage (even k in the low nibble)."""
+    """Integer codes [rows][K] from int8, packed 4-bit (even k in the low nibble) or
+    E2M3 storage (value k in bits 6k .. 6k+5; a pattern that is no integer code
+    in [-7, 7] raises)."""
     c = np.ascontiguousarray(codes, dtype=np.uint8)
+    if bits == E2M3:
+        _, val = _tables()
+        b = c.reshape(c.shape[0], K // 4, 3).astype(np.uint32)
+        word = b[..., 0] | (b[..., 1] << 8) | (b[..., 2] << 16)
+        f = np.stack([(word >> (6 * j)) & 63 for j in range(4)], axis=-1).reshape(c.shape[0], K)
+        out = val[f]
+        if (out == 99).any():
+            raise ValueError("unpack_codes: an E2M3 pattern that is not an integer code in [-7, 7]")
+        return out
     if bits == 8:
         return c.view(np.int8).astype(np.int32).reshape(c.shape[0], K)
     lo = (c & 0xF).astype(np.int32)

@@ -423,3 +423,84 @@ def test_geglu_special_values():
     # gelu_tanh(3) from its definition with tanh evaluated by numpy
     c = np.sqrt(2 / np.pi)
     assert abs(hf[3, 0] - 1.5 * (1 + np.tanh(c * (3 + 0.044715 * 27)))) < 1e-14
+
+
+# ---------------------------------------------------------------- E2M3 storage of the 4-bit codes
+def test_e2m3_values_follow_the_format_definition():
+    # closed forms of FP6 E2M3 (bias 1, subnormals at exponent 0, no inf/NaN)
+    assert oracle.e2m3_value(0b011111) == 7.5     # largest normal: 2^2 x 1.875
+    assert oracle.e2m3_value(0b001000) == 1.0     # smallest normal
+    assert oracle.e2m3_value(0b000001) == 0.125   # smallest subnormal: 1/8
+    assert oracle.e2m3_value(0b000111) == 0.875   # largest subnormal
+    assert oracle.e2m3_value(0b010100) == 3.0
+    assert oracle.e2m3_value(0b011010) == 5.0
+    z = oracle.e2m3_value(0b100000)
+    assert z == 0.0 and math.copysign(1.0, z) < 0
+    pos = [oracle.e2m3_value(c) for c in range(32)]
+    assert all(a < b for a, b in zip(pos, pos[1:]))  # magnitudes grow with the pattern
+    assert all(oracle.e2m3_value(c | 32) == -pos[c] for c in range(32))
+
+
+def test_e2m3_holds_every_4bit_code_exactly():
+    codes = [oracle.e2m3_code(v) for v in range(-7, 8)]
+    assert len(set(codes)) == 15
+    assert [oracle.e2m3_value(c) for c in codes] == [float(v) for v in range(-7, 8)]
+    integral = [c for c in range(64) if oracle.e2m3_value(c) == int(oracle.e2m3_value(c))]
+    assert len(integral) == 16  # the 15 codes and -0
+    with pytest.raises(ValueError):
+        oracle.e2m3_code(8)
+
+
+def test_e2m3_row_fixture():
+    fx = json.load(open(os.path.join(GOLDEN, "e2m3_row.json")))
+    q = np.array([fx["codes"]])
+    assert [oracle.e2m3_code(v) for v in fx["codes"]] == fx["fields"]
+    packed = oracle.pack_e2m3(q)
+    assert list(packed[0]) == fx["bytes"]
+    assert np.array_equal(oracle.unpack_codes(packed, q.shape[1], oracle.E2M3), q)
+    assert [oracle.code_at(packed[0], k, oracle.E2M3) for k in range(q.shape[1])] == fx["codes"]
+
+
+def test_e2m3_bit_positions_one_value_at_a_time():
+    # value k alone in a row sets exactly bits 6k .. 6k+5 of the little-endian bit string
+    K = 16
+    for k in range(K):
+        for v in (1, -3, 7):
+            q = np.zeros((1, K), np.int64)
+            q[0, k] = v
+            row = oracle.pack_e2m3(q)[0]
+            word = int.from_bytes(bytes(row), "little")
+            assert word == oracle.e2m3_code(v) << (6 * k)
+
+
+def test_e2m3_storage_is_the_4bit_quantiser():
+    # packer, prologue and contraction give the same integers as with 4-bit storage
+    rng = np.random.default_rng(51)
+    N, M, K = 9, 5, 256
+    W = rng.normal(0, 0.02, (N, K)).astype(np.float32)
+    a = rng.uniform(0.5, 2.0, K).astype(np.float32)
+    c4, s4 = oracle.pack_weights(W, a, 0, 64, 4)
+    c6, s6 = oracle.pack_weights(W, a, 0, 64, oracle.E2M3)
+    assert c6.shape == (N, 3 * K // 4)
+    assert np.array_equal(s4, s6)
+    assert np.array_equal(oracle.unpack_codes(c4, K, 4), oracle.unpack_codes(c6, K, oracle.E2M3))
+    x = _bf16(rng.normal(0, 1, (M, K)))
+    g = rng.uniform(0.5, 1.5, K).astype(np.float32)
+    a4, sa4 = oracle.prologue(x, g, 1e-6, None, 0, 64, 4)
+    a6, sa6 = oracle.prologue(x, g, 1e-6, None, 0, 64, oracle.E2M3)
+    assert np.array_equal(sa4, sa6)
+    qa = oracle.unpack_codes(a4, K, 4)
+    assert np.array_equal(qa, oracle.unpack_codes(a6, K, oracle.E2M3))
+    acc6 = oracle.gemm_i32(a6, oracle.E2M3, c6, oracle.E2M3, K)
+    qw = oracle.unpack_codes(c4, K, 4)
+    assert np.array_equal(acc6, (qa.astype(np.int64) @ qw.astype(np.int64).T).astype(np.int32))
+    u4 = oracle.unfold_weights(c4, s4, K, a, 0, 64, 4)
+    u6 = oracle.unfold_weights(c6, s6, K, a, 0, 64, oracle.E2M3)
+    assert np.array_equal(u4, u6)
+
+
+def test_e2m3_unpack_rejects_non_code_patterns():
+    row = np.zeros((1, 3), np.uint8)
+    row[0, 0] = 0b011111  # 7.5 in field 0: no integer code
+    with pytest.raises(ValueError):
+        oracle.unpack_codes(row, 4, oracle.E2M3)
