@@ -539,6 +539,53 @@ def describe(name, wl):
             f"hblock={wl.hblock}, weights warm in HBM")
 
 
+def vendor_gemms(steps=200):
+    """Context only: the vendor GEMMs (hipBLASLt through torch: int8 torch._int_mm with an int32 result, fp8
+    e4m3 torch._scaled_mm with a bf16 result, bf16 matmul) on the four prefill layers' M x N x K, next to this
+    library's fq_gemm on the same shapes.  Operands are random codes; the library GEMMs do no quantisation
+    and no epilogue beyond their own output type, so they do less work than fq_gemm."""
+    import torch
+    import synth
+    out = {}
+    for name in ("qkv_w8a8", "down_w8a8", "gateup_w4a4", "down_w4a4"):
+        wl = synth.make_workload(name)
+        M, N, K = wl.M, wl.N, wl.K
+        ops = 2.0 * M * N * K
+        site = site_for(wl)
+        x = site.upload(wl.x)
+        res = site.upload(wl.residual) if wl.residual is not None else None
+        y = site.empty_out(M)
+        site.workspace(M)
+        site.linear(x, residual=res, y=y)
+        codes, scales = site.workspace_codes(M)
+
+        def timed(step):
+            warm_up(step, 20)
+            return min(graph_steps(step, steps)[0] for _ in range(3))
+        r = {"shape": f"M={M} N={N} K={K}"}
+        ms = timed(lambda: site.gemm(codes, scales, M, residual=res, y=y))
+        r[f"fq_gemm W{wl.wbits}A{wl.abits} (bf16 out, fused epilogue)"] = {"us": ms * 1e3, "tops": ops / ms / 1e9}
+        a = torch.randint(-127, 128, (M, K), dtype=torch.int8, device="cuda")
+        w = torch.randint(-127, 128, (N, K), dtype=torch.int8, device="cuda")
+        ms = timed(lambda: torch._int_mm(a, w.t()))
+        r["torch._int_mm int8 (int32 out)"] = {"us": ms * 1e3, "tops": ops / ms / 1e9}
+        try:
+            af = torch.randn(M, K, device="cuda").to(torch.float8_e4m3fn)
+            wf = torch.randn(N, K, device="cuda").to(torch.float8_e4m3fn)
+            one = torch.ones((), device="cuda")
+            ms = timed(lambda: torch._scaled_mm(af, wf.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16))
+            r["torch._scaled_mm fp8 e4m3 (bf16 out)"] = {"us": ms * 1e3, "tops": ops / ms / 1e9}
+        except RuntimeError as e:
+            r["torch._scaled_mm fp8 e4m3 (bf16 out)"] = f"unavailable: {str(e)[:120]}"
+        ab = torch.randn(M, K, device="cuda", dtype=torch.bfloat16)
+        wb = torch.randn(N, K, device="cuda", dtype=torch.bfloat16)
+        ms = timed(lambda: torch.matmul(ab, wb.t()))
+        r["torch.matmul bf16"] = {"us": ms * 1e3, "tflops": ops / ms / 1e9}
+        out[name] = r
+        del a, w, ab, wb
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -552,6 +599,8 @@ def main():
     ap.add_argument("--no-ceilings", action="store_true", help="skip the measured MFMA and HBM-read ceilings")
     ap.add_argument("--no-clocks", action="store_true", help="skip the amd-smi clock and power samples")
     ap.add_argument("--ceilings-only", action="store_true", help="print the measured ceilings only")
+    ap.add_argument("--vendor-only", action="store_true",
+                    help="print the vendor GEMMs (hipBLASLt via torch) next to fq_gemm on the prefill shapes")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} requested, but this build measures one GPU only: the FoldQuant "
@@ -567,6 +616,9 @@ def main():
     if args.ceilings_only:
         print(json.dumps({"ceilings": measure_ceilings()}), flush=True)
         return
+    if args.vendor_only:
+        print(json.dumps({"vendor_gemms": vendor_gemms()}), flush=True)
+        return
 
     clocks = {}
     if not args.no_clocks:
@@ -578,7 +630,7 @@ def main():
                 "achieved": achieved, "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
                 "unit_note": "tera integer operations per second (2*M*N*K per GEMM)",
                 "frac": achieved / PEAK_INT8_TOPS,
-                "traffic": load_traffic(f"gemm:{args.workload}", ("fq_gemm.hip", "fq_device.h")),
+                "traffic": load_traffic(f"gemm:{args.workload}", ("fq_gemm.hip", "fq_ring.h", "fq_device.h")),
                 "traffic_unit": "bytes per launch (scaled FETCH_SIZE + WRITE_SIZE)",
                 "algorithmic_bytes": gemm_bytes(wl)}
     secondary = []

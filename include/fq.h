@@ -17,7 +17,8 @@
  *
  * qmax is 127 for 8-bit codes and 7 for 4-bit codes (the page's "15 activation
  * levels").  4-bit codes are packed two per byte with the even k in the low
- * nibble.  Weight rows are folded into the same frame on the host by
+ * nibble.  Code width FQ_CODES_E2M3 (6) is a second storage of the same 4-bit
+ * codes (see below).  Weight rows are folded into the same frame on the host by
  * fq_pack_weights: u_n = R_b(a . w_n) (fold before) or a . R_b(w_n) (fold
  * after), then per-row symmetric round-to-nearest-even with s_n = max|u_n|/qmax.
  *
@@ -52,7 +53,8 @@
  *     fq_prologue (of 64 when K > 32768) and of 128 for fq_pack_weights,
  *     fq_dequant_rows, fq_gemm and fq_linear;
  *     hblock a power of two in [1, 256] dividing K (1 = no rotation); bits in
- *     {4, 8} for both weights and activations (W8A8, W4A4, W4A8, W8A4).
+ *     {4, 8} for both weights and activations (W8A8, W4A4, W4A8, W8A4), or 6
+ *     (FQ_CODES_E2M3) for both of a GEMM's operands.
  *   - Alignment: bf16 rows (x, residual, y) need a 16-byte aligned base and a
  *     leading dimension that is a multiple of 8 elements; code buffers, gamma,
  *     ascale, scales and bias need a 16-byte aligned base.
@@ -69,7 +71,21 @@
 extern "C" {
 #endif
 
-#define FQ_ABI_VERSION 1
+#define FQ_ABI_VERSION 2
+
+/* Code width 6: the 4-bit codes (integers in [-7, 7], qmax 7, quantised exactly
+ * as with width 4) stored as OCP FP6 E2M3 numbers -- sign bit 5, exponent bits
+ * 4..3 with bias 1, mantissa bits 2..0 -- which hold each of those integers
+ * exactly.  Value k of a row occupies bits 6k .. 6k+5 of the row's bytes read
+ * as one little-endian bit string: 3K/4 bytes per row.  In this form a W4A4
+ * GEMM runs on gfx950's FP6 matrix instruction (v_mfma_scale_f32_16x16x128_f8f6f4,
+ * twice the rate of the int8 one) with float32 sums that stay exact integers
+ * (|sum| <= 49 K < 2^24), so its results equal the 4-bit path's bit for bit.
+ * Accepted by fq_pack_weights, fq_dequant_rows, fq_prologue, and by the GEMM
+ * entry points when both abits and wbits are 6 (mixing 6 with 4 or 8 is
+ * FQ_ERR_UNSUPPORTED).  Every M runs on the tiled kernel: for decode-sized M
+ * the 4-bit storage streams a third fewer weight bytes. */
+#define FQ_CODES_E2M3 6
 
 typedef enum {
     FQ_OK = 0,
@@ -109,8 +125,8 @@ fq_status fq_test_hook(const char* spec);
 
 /* ------------------------------------------------------------------ host, synchronous */
 
-/* Bytes of one code matrix of rows x K codes at `bits` bits (rows*K or rows*K/2);
- * 0 on bad arguments. */
+/* Bytes of one code matrix of rows x K codes at `bits` bits (rows*K, rows*K/2,
+ * or rows*3K/4 for FQ_CODES_E2M3); 0 on bad arguments. */
 size_t fq_weight_bytes(int32_t N, int32_t K, int32_t wbits);
 size_t fq_act_bytes(int32_t M, int32_t K, int32_t abits);
 
@@ -126,7 +142,8 @@ fq_status fq_fold_gain(const float* gamma, const float* ascale, int32_t K, float
  *   fold_after 0: u_n = R_b(a . w_n); 1: u_n = a . R_b(w_n) -- must match the
  *              prologue's fold order (or the gain fold, which is fold before)
  *   hblock     Hadamard block b (1 = no rotation)
- *   codes_out  host, fq_weight_bytes(N, K, wbits) bytes: int8 [N][K] or packed [N][K/2]
+ *   codes_out  host, fq_weight_bytes(N, K, wbits) bytes: int8 [N][K], packed [N][K/2],
+ *              or E2M3 [N][3K/4] (wbits 6)
  *   wscale_out host float32 [N]: s_n = (float)(max|u_n| / qmax)
  * The fold runs in float64; codes are rounded (ties to even) against the stored
  * float32 scale and clamped to +-qmax. */
@@ -159,7 +176,7 @@ fq_status fq_dequant_rows(const void* codes, const float* wscale, int32_t N, int
  *   eps          RMSNorm epsilon (ignored without gamma)
  *   ascale       device float32 [K] explicit smoothing divide, or NULL
  *   fold_after   0: divide before the rotation; 1: after it
- *   act_codes    device, fq_act_bytes(M, K, abits) bytes, row stride K (or K/2) bytes
+ *   act_codes    device, fq_act_bytes(M, K, abits) bytes, row stride K, K/2 or 3K/4 bytes
  *   act_scale    device float32 [M] */
 fq_status fq_prologue(const void* x_bf16, int32_t M, int32_t K, int64_t ldx,
                       const float* gamma_folded, float eps, const float* ascale,
@@ -176,7 +193,8 @@ fq_status fq_prologue(const void* x_bf16, int32_t M, int32_t K, int64_t ldx,
  *   acc_i32              device int32 [M][N] (row stride N) receiving the exact
  *                        accumulators, or NULL (diagnostic output)
  * M <= 32 runs the weight-streaming GEMV kernel, larger M the tiled MFMA kernel;
- * both give identical results. */
+ * both give identical results.  E2M3 codes (abits = wbits = 6) run the FP6
+ * tiled kernel for every M, with the same results as the 4-bit codes. */
 fq_status fq_gemm(const void* act_codes, const float* act_scale, int32_t M, int32_t abits,
                   const void* w_codes, const float* wscale, int32_t N, int32_t K, int32_t wbits,
                   const float* bias, const void* residual_bf16, int64_t ldr,

@@ -47,6 +47,8 @@ def rand_codes(rng, rows, K, bits, extreme=False):
         q = rng.integers(-qmax, qmax + 1, size=(rows, K))
     if bits == 8:
         return q.astype(np.int8).view(np.uint8)
+    if bits == oracle.E2M3:
+        return oracle.pack_e2m3(q)
     return ((q[:, 0::2] & 0xF) | ((q[:, 1::2] & 0xF) << 4)).astype(np.uint8)
 
 

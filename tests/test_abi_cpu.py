@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(_binding.SIGNATURES), "binding and header disagree"
-    assert fq.abi_version() == 1
+    assert fq.abi_version() == 2
 
 
 def test_sizes():
@@ -44,11 +44,13 @@ def test_sizes():
     assert fq.fq_weight_bytes(32768, 2048, 4) == 32768 * 1024
     assert fq.fq_act_bytes(816, 16384, 4) == 816 * 8192
     assert fq.fq_weight_bytes(0, 64, 8) == 0 and fq.fq_weight_bytes(4, 64, 3) == 0
+    assert fq.fq_weight_bytes(32768, 2048, fq.E2M3) == 32768 * 1536
+    assert fq.fq_act_bytes(816, 16384, fq.E2M3) == 816 * 12288
     ws = fq.fq_linear_workspace_bytes(1024, 3584, 8)
     assert ws >= 1024 * 3584 + 4 * 1024 and ws % 256 == 0
 
 
-@pytest.mark.parametrize("wbits", [8, 4])
+@pytest.mark.parametrize("wbits", [8, 4, 6])
 @pytest.mark.parametrize("fold_after", [0, 1])
 @pytest.mark.parametrize("hblock", [1, 2, 8, 32, 64, 128, 256])
 @pytest.mark.parametrize("with_a", [False, True])
@@ -72,9 +74,26 @@ def test_host_packer_matches_oracle_on_workload_shapes():
     c2, s2 = oracle.pack_weights(wl.W, wl.ascale, 0, wl.hblock, 8)
     assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
     wl = synth.make_workload("gateup_w4a4", N=256)
-    c1, s1 = fq.fq_pack_weights(wl.W, wl.ascale, 0, wl.hblock, 4)
-    c2, s2 = oracle.pack_weights(wl.W, wl.ascale, 0, wl.hblock, 4)
-    assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
+    for bits in (4, fq.E2M3):
+        c1, s1 = fq.fq_pack_weights(wl.W, wl.ascale, 0, wl.hblock, bits)
+        c2, s2 = oracle.pack_weights(wl.W, wl.ascale, 0, wl.hblock, bits)
+        assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
+
+
+def test_e2m3_storage_holds_the_4bit_codes():
+    """The E2M3 rows carry the 4-bit packer's integers, scale for scale, and
+    dequantise to the same floats."""
+    rng = np.random.default_rng(61)
+    N, K = 40, 1024
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    a = rng.uniform(0.3, 3.0, K).astype(np.float32)
+    c4, s4 = fq.fq_pack_weights(W, a, 1, 64, 4)
+    c6, s6 = fq.fq_pack_weights(W, a, 1, 64, fq.E2M3)
+    assert c6.shape == (N, 3 * K // 4) and np.array_equal(s4, s6)
+    assert np.array_equal(oracle.unpack_codes(c4, K, 4), oracle.unpack_codes(c6, K, oracle.E2M3))
+    d4 = fq.fq_dequant_rows(c4, s4, K, a, 1, 64, 4)
+    d6 = fq.fq_dequant_rows(c6, s6, K, a, 1, 64, fq.E2M3)
+    assert np.array_equal(d4, d6)
 
 
 def _ulp_diff(a32, b32):
@@ -220,7 +239,9 @@ def _gemm(**kw):
     (dict(ldy=64), 2, "ldy=64 < N=128"),
     (dict(res=DEV, ldr=64), 2, "ldr=64 < N=128"),
     (dict(res=DEV, ldr=132), 4, "ldr=132 is not a multiple of 8"),
-    (dict(wbits=6), 3, "wbits=6"),
+    (dict(wbits=5), 3, "wbits=5"),
+    (dict(wbits=6), 3, "abits=8 with wbits=6: E2M3 codes"),
+    (dict(abits=6, wbits=4), 3, "abits=6 with wbits=4"),
     (dict(w=BAD), 4, "w_codes is not 16-byte aligned"),
     (dict(acc=BAD), 4, "acc_i32 is not 16-byte aligned"),
     (dict(K=0), 2, "K=0"),

@@ -5,7 +5,7 @@ hand-written HIP kernels behind the C ABI declared in include/fq.h.  This
 package only loads that library and marshals arguments; torch provides device
 memory and streams.
 """
-from ._binding import (FqError, abi_version, fq_act_bytes, fq_dequant_rows, fq_device_init, fq_fold_gain, fq_geglu,
+from ._binding import (E2M3, FqError, abi_version, fq_act_bytes, fq_dequant_rows, fq_device_init, fq_fold_gain, fq_geglu,
                        fq_gemm, fq_gemm_heads, fq_test_hook,
                        fq_linear, fq_linear_heads, fq_linear_noalloc, fq_linear_noalloc_max_bytes,
                        fq_linear_workspace_bytes, fq_pack_weights, fq_prologue, fq_weight_bytes, last_error,
@@ -13,7 +13,7 @@ from ._binding import (FqError, abi_version, fq_act_bytes, fq_dequant_rows, fq_d
 from .site import DeviceSite
 
 __all__ = [
-    "FqError", "abi_version", "fq_act_bytes", "fq_device_init", "fq_fold_gain", "fq_test_hook", "fq_geglu",
+    "E2M3", "FqError", "abi_version", "fq_act_bytes", "fq_device_init", "fq_fold_gain", "fq_test_hook", "fq_geglu",
     "fq_gemm", "fq_gemm_heads", "fq_linear", "fq_linear_heads", "fq_linear_noalloc", "fq_linear_noalloc_max_bytes",
     "fq_linear_workspace_bytes",
     "fq_pack_weights", "fq_dequant_rows", "fq_prologue", "fq_weight_bytes", "last_error", "lib", "DeviceSite",

@@ -17,6 +17,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 # FQ_LIB selects another build of the same library (the host-sanitizer build)
 LIB_PATH = os.environ.get("FQ_LIB") or os.path.join(HERE, "libfq.so")
 
+E2M3 = 6  # FQ_CODES_E2M3: the 4-bit codes stored as FP6 E2M3 (include/fq.h)
+
 FQ_OK = 0
 _STATUS = {0: "FQ_OK", 1: "FQ_ERR_ARG", 2: "FQ_ERR_SHAPE", 3: "FQ_ERR_UNSUPPORTED", 4: "FQ_ERR_ALIGN",
            5: "FQ_ERR_DEVICE"}
@@ -125,7 +127,7 @@ def fq_fold_gain(gamma: np.ndarray, ascale: Optional[np.ndarray]) -> np.ndarray:
 
 
 def fq_pack_weights(W: np.ndarray, ascale: Optional[np.ndarray], fold_after: int, hblock: int, wbits: int):
-    """Host packer; returns (codes uint8 [N][K or K/2], wscale float32 [N])."""
+    """Host packer; returns (codes uint8 [N][K, K/2 or 3K/4 (E2M3)], wscale float32 [N])."""
     W = np.ascontiguousarray(W, dtype=np.float32)
     N, K = W.shape
     a = None if ascale is None else np.ascontiguousarray(ascale, dtype=np.float32)

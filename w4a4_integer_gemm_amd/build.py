@@ -15,7 +15,7 @@ LIB = os.path.join(HERE, "libfq.so")
 CEILING_LIB = os.path.join(HERE, "libfq_ceiling.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["fq_api.cpp", "fq_pack.cpp", "fq_prologue.hip", "fq_gemm.hip", "fq_gemv.hip", "fq_geglu.hip",
+SOURCES = ["fq_api.cpp", "fq_pack.cpp", "fq_prologue.hip", "fq_gemm.hip", "fq_gemm_fp6.hip", "fq_gemv.hip", "fq_geglu.hip",
            "fq_noalloc.hip", "fq_decode1.hip"]
 # the benchmark's ceiling probes: a library of their own, outside the layer's ABI
 CEILING_SOURCES = ["fq_ceiling.hip"]

@@ -144,8 +144,9 @@ constexpr int32_t kGemmK = 128;        // one k stage of the GEMM
 
 // Checks shared by the prologue, the GEMM and the packer.  Returns FQ_OK or the failure.
 fq_status check_bits(const char* fn, const char* name, int32_t bits) {
-    if (bits != 8 && bits != 4)
-        return fail(FQ_ERR_UNSUPPORTED, fmt("%s: %s=%d is not a supported code width (4 or 8)", fn, name, bits));
+    if (bits != 8 && bits != 4 && bits != FQ_CODES_E2M3)
+        return fail(FQ_ERR_UNSUPPORTED,
+                    fmt("%s: %s=%d is not a supported code width (4, 8, or 6 for E2M3)", fn, name, bits));
     return FQ_OK;
 }
 
@@ -218,6 +219,9 @@ fq_status validate_gemm(const char* fn, const void* act, const float* act_scale,
     FQ_TRY(check_k(fn, K, kGemmK));
     FQ_TRY(check_bits(fn, "abits", abits));
     FQ_TRY(check_bits(fn, "wbits", wbits));
+    if ((abits == FQ_CODES_E2M3) != (wbits == FQ_CODES_E2M3))
+        return fail(FQ_ERR_UNSUPPORTED, fmt("%s: abits=%d with wbits=%d: E2M3 codes (6) need both operands in E2M3",
+                                            fn, abits, wbits));
     if (head_dim > 0) {
         if (head_dim % 8)
             return fail(FQ_ERR_SHAPE, fmt("%s: head_dim=%d is not a multiple of 8", fn, head_dim));
@@ -248,7 +252,8 @@ fq_status device_status(const char* fn, hipError_t e) {
 }
 
 size_t code_bytes(int32_t rows, int32_t K, int32_t bits) {
-    if (rows < 1 || K < 2 || K % 2 || (bits != 4 && bits != 8)) return 0;
+    if (rows < 1 || K < 4 || K % 4 || (bits != 4 && bits != 8 && bits != FQ_CODES_E2M3)) return 0;
+    if (bits == FQ_CODES_E2M3) return size_t(rows) * size_t(3 * (K / 4));
     return bits == 8 ? size_t(rows) * size_t(K) : size_t(rows) * size_t(K / 2);
 }
 
@@ -260,7 +265,9 @@ fq_status prepare(const char* fn, const fq::DeviceInfo** info) {
 }
 
 fq_status run_gemm(const char* fn, const fq::GemmArgs& g, const fq::DeviceInfo& dev, hipStream_t stream) {
-    hipError_t e = g.M <= fq::kGemvMaxM ? fq::launch_gemv(g, dev, stream) : fq::launch_gemm(g, stream);
+    hipError_t e = g.abits == FQ_CODES_E2M3   ? fq::launch_gemm_e2m3(g, stream)
+                   : g.M <= fq::kGemvMaxM ? fq::launch_gemv(g, dev, stream)
+                                          : fq::launch_gemm(g, stream);
     return device_status(fn, e);
 }
 

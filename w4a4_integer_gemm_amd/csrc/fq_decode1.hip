@@ -23,9 +23,9 @@
 // row group per workgroup 27.5 us, three 29.3 us, four 32.7 us (the register
 // file then holds fewer workgroups).
 //
-// Taken when M = 1, K <= 4096 (8 values per lane over 512 lanes) and the
-// Hadamard block is 32, 64 or 128 (a block spans at most 16 lanes); other
-// one-token calls take the two launches.
+// Taken when M = 1, K <= 4096 (8 values per lane over 512 lanes), the codes
+// are 4- or 8-bit and the Hadamard block is 32, 64 or 128 (a block spans at
+// most 16 lanes); other one-token calls take the two launches.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -173,7 +173,8 @@ hipError_t launch_bits(const PrologueArgs& p, const GemmArgs& g, int per, hipStr
 
 bool decode1_eligible(const PrologueArgs& p, const GemmArgs& g) {
     if (hooks().decode1_off.load(std::memory_order_relaxed)) return false;
-    return g.M == 1 && p.M == 1 && g.K <= kMaxK && (p.hblock == 32 || p.hblock == 64 || p.hblock == 128);
+    return g.M == 1 && p.M == 1 && g.abits != 6 && g.K <= kMaxK &&
+           (p.hblock == 32 || p.hblock == 64 || p.hblock == 128);
 }
 
 hipError_t launch_decode1(const PrologueArgs& p, const GemmArgs& g, hipStream_t stream) {

@@ -95,6 +95,8 @@ hipError_t init_scratch_device(DeviceInfo& d);
 // are validated by the caller; a launch makes no other HIP call.
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t stream);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
+// The FP6 kernel for E2M3 codes (abits = wbits = 6), every M.
+hipError_t launch_gemm_e2m3(const GemmArgs& g, hipStream_t stream);
 hipError_t launch_gemv(const GemmArgs& a, const DeviceInfo& dev, hipStream_t stream);
 // One-token fq_linear in one launch (fq_decode1.hip): whether the shape takes
 // it, and the launch (prologue arguments and GEMM arguments of the same call).

@@ -42,10 +42,33 @@ void rotate_row(double* u, int32_t K, int32_t b) {
     for (int32_t k = 0; k < K; ++k) u[k] *= norm;
 }
 
+size_t code_row_bytes(int32_t K, int32_t bits) {
+    return bits == 8 ? size_t(K) : bits == FQ_CODES_E2M3 ? size_t(3 * (K / 4)) : size_t(K / 2);
+}
+
+// FP6 E2M3 pattern of an integer code |q| <= 7: the exponent is the position of
+// the leading one plus the bias 1, the three mantissa bits the ones below it
+// (q = 2^(e-1) (1 + m/8)); 0 is the zero pattern.
+uint32_t e2m3_pattern(int32_t q) {
+    if (q == 0) return 0;
+    const uint32_t sign = q < 0 ? 32u : 0u;
+    const int32_t mag = q < 0 ? -q : q;
+    const int32_t e = mag >= 4 ? 3 : mag >= 2 ? 2 : 1;
+    const int32_t m = ((mag * 8) >> (e - 1)) - 8;
+    return sign | uint32_t(e << 3) | uint32_t(m);
+}
+
+// Value of an E2M3 pattern (exponent 0 is subnormal: m/8).
+double e2m3_number(uint32_t f) {
+    const int32_t e = (f >> 3) & 3, m = f & 7;
+    const double mag = e == 0 ? m / 8.0 : std::ldexp(1.0 + m / 8.0, e - 1);
+    return (f & 32) ? -mag : mag;
+}
+
 void pack_rows(const float* W, int32_t n0, int32_t n1, int32_t K, const float* a, int32_t fold_after, int32_t b,
                int32_t bits, uint8_t* codes, float* wscale) {
     const int32_t qmax = bits == 8 ? 127 : 7;
-    const size_t row_bytes = bits == 8 ? size_t(K) : size_t(K / 2);
+    const size_t row_bytes = code_row_bytes(K, bits);
     std::vector<double> u(K);
     std::vector<int32_t> q(K);
     for (int32_t n = n0; n < n1; ++n) {
@@ -68,6 +91,15 @@ void pack_rows(const float* W, int32_t n0, int32_t n1, int32_t K, const float* a
         uint8_t* row = codes + size_t(n) * row_bytes;
         if (bits == 8) {
             for (int32_t k = 0; k < K; ++k) row[k] = static_cast<uint8_t>(static_cast<int8_t>(q[k]));
+        } else if (bits == FQ_CODES_E2M3) {
+            // four 6-bit fields -> three bytes, value k at bits 6k .. 6k+5
+            for (int32_t j = 0; j < K / 4; ++j) {
+                uint32_t w = 0;
+                for (int32_t i = 0; i < 4; ++i) w |= e2m3_pattern(q[4 * j + i]) << (6 * i);
+                row[3 * j + 0] = uint8_t(w);
+                row[3 * j + 1] = uint8_t(w >> 8);
+                row[3 * j + 2] = uint8_t(w >> 16);
+            }
         } else {
             for (int32_t j = 0; j < K / 2; ++j)
                 row[j] = static_cast<uint8_t>((q[2 * j] & 0xF) | ((q[2 * j + 1] & 0xF) << 4));
@@ -80,20 +112,24 @@ void pack_rows(const float* W, int32_t n0, int32_t n1, int32_t K, const float* a
 // R(v/a) (fold after); R is its own inverse, so this undoes the packer's fold.
 void dequant_rows(const uint8_t* codes, const float* wscale, int32_t n0, int32_t n1, int32_t K, const float* a,
                   int32_t fold_after, int32_t b, int32_t bits, float* W) {
-    const size_t row_bytes = bits == 8 ? size_t(K) : size_t(K / 2);
+    const size_t row_bytes = code_row_bytes(K, bits);
     std::vector<double> v(K);
     for (int32_t n = n0; n < n1; ++n) {
         const uint8_t* row = codes + size_t(n) * row_bytes;
         const double s = static_cast<double>(wscale[n]);
         for (int32_t k = 0; k < K; ++k) {
-            int32_t q;
+            double q;
             if (bits == 8) {
                 q = static_cast<int8_t>(row[k]);
+            } else if (bits == FQ_CODES_E2M3) {
+                const uint8_t* t = row + 3 * (k / 4);
+                const uint32_t w = uint32_t(t[0]) | (uint32_t(t[1]) << 8) | (uint32_t(t[2]) << 16);
+                q = e2m3_number((w >> (6 * (k % 4))) & 63u);
             } else {
                 const int32_t nib = (row[k / 2] >> (4 * (k & 1))) & 0xF;
                 q = nib >= 8 ? nib - 16 : nib;
             }
-            v[k] = s * static_cast<double>(q);
+            v[k] = s * q;
         }
         if (a && fold_after)
             for (int32_t k = 0; k < K; ++k) v[k] /= static_cast<double>(a[k]);
@@ -113,8 +149,8 @@ fq_status check_rows(const char* fn, int32_t N, int32_t K, const float* ascale, 
         fq::set_error(buf);
         return s;
     };
-    if (wbits != 8 && wbits != 4) {
-        snprintf(buf, sizeof buf, "%s: wbits=%d is not a supported code width (4 or 8)", fn, wbits);
+    if (wbits != 8 && wbits != 4 && wbits != FQ_CODES_E2M3) {
+        snprintf(buf, sizeof buf, "%s: wbits=%d is not a supported code width (4, 8, or 6 for E2M3)", fn, wbits);
         return fail(FQ_ERR_UNSUPPORTED);
     }
     if (N < 1) {

@@ -72,7 +72,7 @@ __global__ __launch_bounds__(kMaxThreads) void prologue_kernel(const uint16_t* _
     __shared__ float red_f[kMaxWaves];
     const int m = blockIdx.x;
     const int c = threadIdx.x;
-    uint8_t* const row = codes + int64_t(m) * (ABITS == 8 ? K : K / 2);
+    uint8_t* const row = codes + int64_t(m) * (ABITS == 8 ? K : ABITS == 6 ? K / 4 * 3 : K / 2);
     const float s = quantise_token<E, ABITS, NORM, AMODE, LOG2B>(
         x + int64_t(m) * ldx, K, gamma, eps, ascale, rs, c, int(blockDim.x) >> 6, red_d, red_f,
         [&](int off, auto v) {
@@ -92,7 +92,7 @@ __global__ __launch_bounds__(kMaxThreads) void prologue_kernel(const uint16_t* _
 
 template <int E, int ABITS, bool NORM, int AMODE, int LOG2B>
 hipError_t launch_e(dim3 grid, dim3 block, hipStream_t st, const PrologueArgs& a, float rs) {
-    if constexpr ((1 << LOG2B) > 16 * E) {
+    if constexpr ((1 << LOG2B) > 16 * E || (ABITS == 6 && E < 16)) {
         return hipErrorInvalidValue;  // not chosen by launch_prologue
     } else {
         hipLaunchKernelGGL((prologue_kernel<E, ABITS, NORM, AMODE, LOG2B>), grid, block, 0, st, a.x, a.K, a.ldx,
@@ -139,13 +139,13 @@ hipError_t launch_modes(dim3 grid, dim3 block, hipStream_t st, const PrologueArg
 // steps, and halving a lane's share shortens it (measured on the qkv prologue,
 // K = 3584: 7.0 -> 6.0 us for 1024 tokens, 4.0 -> 3.4 us for one; 8 per lane
 // gained nothing more); 32 up to K = 32768 (one pass of at most 1024 lanes),
-// 64 beyond.
+// 64 beyond.  E2M3 codes take at least 16 (they leave in 12-byte groups).
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t stream) {
     // (a Hadamard block spans at most 16 lanes: 8 values per lane only for b <= 128)
-    const int E = a.M <= kFewTokens && a.K <= kFewTokensMaxK && a.hblock <= 128 ? 8
-                  : a.K <= 8192                                         ? 16
-                  : a.K > 32768                                         ? 64
-                                                                        : 32;
+    const int E = a.M <= kFewTokens && a.K <= kFewTokensMaxK && a.hblock <= 128 && a.abits != 6 ? 8
+                  : a.K <= 8192                                                         ? 16
+                  : a.K > 32768                                                         ? 64
+                                                                                        : 32;
     const int nlanes = a.K / E;
     const int T = (nlanes + 63) / 64 * 64;
     if (T > kMaxThreads) return hipErrorInvalidValue;
@@ -154,10 +154,16 @@ hipError_t launch_prologue(const PrologueArgs& a, hipStream_t stream) {
     if (E == 8)
         return a.abits == 8 ? launch_modes<8, 8>(grid, block, stream, a, rs) : launch_modes<8, 4>(grid, block, stream, a, rs);
     if (E == 16)
-        return a.abits == 8 ? launch_modes<16, 8>(grid, block, stream, a, rs) : launch_modes<16, 4>(grid, block, stream, a, rs);
+        return a.abits == 8   ? launch_modes<16, 8>(grid, block, stream, a, rs)
+               : a.abits == 6 ? launch_modes<16, 6>(grid, block, stream, a, rs)
+                              : launch_modes<16, 4>(grid, block, stream, a, rs);
     if (E == 32)
-        return a.abits == 8 ? launch_modes<32, 8>(grid, block, stream, a, rs) : launch_modes<32, 4>(grid, block, stream, a, rs);
-    return a.abits == 8 ? launch_modes<64, 8>(grid, block, stream, a, rs) : launch_modes<64, 4>(grid, block, stream, a, rs);
+        return a.abits == 8   ? launch_modes<32, 8>(grid, block, stream, a, rs)
+               : a.abits == 6 ? launch_modes<32, 6>(grid, block, stream, a, rs)
+                              : launch_modes<32, 4>(grid, block, stream, a, rs);
+    return a.abits == 8   ? launch_modes<64, 8>(grid, block, stream, a, rs)
+           : a.abits == 6 ? launch_modes<64, 6>(grid, block, stream, a, rs)
+                          : launch_modes<64, 4>(grid, block, stream, a, rs);
 }
 
 }  // namespace fq

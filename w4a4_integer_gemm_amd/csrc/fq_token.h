@@ -259,6 +259,7 @@ __device__ __forceinline__ float quantise_loaded(const TokenLoad<E, NORM>& t, in
                                                  int nwaves, double* red_d, float* red_f, Store store) {
     constexpr int hblock = 1 << LOG2B;
     static_assert(hblock <= 16 * E, "a Hadamard block spans at most 16 lanes (cross-lane distances 1 .. 8)");
+    static_assert(ABITS != 6 || E >= 16, "E2M3 codes leave in groups of 16 values (12 bytes)");
     constexpr int qmax = ABITS == 8 ? 127 : 7;
     const int lane = c & 63;
     const int wave = c >> 6;
@@ -341,7 +342,7 @@ __device__ __forceinline__ float quantise_loaded(const TokenLoad<E, NORM>& t, in
     // branch around every element's fallback divide)
     auto quantise = [&](auto fast_tag) {
         constexpr bool kFast = decltype(fast_tag)::value;
-        // codes per store: at most 16 bytes of them
+        // codes per store: at most 16 bytes of them (E2M3: 16 or 32 values, 12 or 24 bytes)
         constexpr int G = ABITS == 8 ? (E < 16 ? E : 16) : (E < 32 ? E : 32);
 #pragma unroll
         for (int grp = 0; grp < E / G; ++grp) {
@@ -359,7 +360,29 @@ __device__ __forceinline__ float quantise_loaded(const TokenLoad<E, NORM>& t, in
                 }
                 t[i] = round_to_code_bits(qf);
             }
-            if (ABITS == 8) {
+            if constexpr (ABITS == 6) {
+                // E2M3: the rounded codes are exact float integers in [-7, 7]; the
+                // converter interleaves its two sources (field 2i from the first,
+                // 2i + 1 from the second), so even values go first and odd second,
+                // which puts value j of the group in bits 6j .. 6j+5
+                v16f ev, od;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    ev[i] = 2 * i < G ? __uint_as_float(t[2 * i < G ? 2 * i : 0]) - 0x1.8p23f : 0.0f;
+                    od[i] = 2 * i + 1 < G ? __uint_as_float(t[2 * i + 1 < G ? 2 * i + 1 : 0]) - 0x1.8p23f : 0.0f;
+                }
+                const v6i f = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, 1.0f);
+                const int off = (E * c + G * grp) / 4 * 3;
+                if constexpr (G == 32) {
+                    store(off, make_uint2(uint32_t(f[0]), uint32_t(f[1])));
+                    store(off + 8, make_uint2(uint32_t(f[2]), uint32_t(f[3])));
+                    store(off + 16, make_uint2(uint32_t(f[4]), uint32_t(f[5])));
+                } else {
+                    store(off, uint32_t(f[0]));
+                    store(off + 4, uint32_t(f[1]));
+                    store(off + 8, uint32_t(f[2]));
+                }
+            } else if (ABITS == 8) {
                 uint32_t w[G / 4];
 #pragma unroll
                 for (int i = 0; i < G / 4; ++i) {

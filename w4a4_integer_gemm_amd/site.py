@@ -34,7 +34,8 @@ class DeviceSite:
                  fold_after: int = 0, fold_into_gain: bool = True, bias=None, eps: float = 1e-6,
                  device="cuda", codes=None, wscale=None):
         import torch
-        self.N, self.K = W.shape if W is not None else (codes.shape[0], codes.shape[1] * (8 // wbits))
+        # (code bytes per row: K * bits / 8, with 6 bits for the E2M3 storage)
+        self.N, self.K = W.shape if W is not None else (codes.shape[0], codes.shape[1] * 8 // wbits)
         self.hblock, self.wbits, self.abits = hblock, wbits, abits
         self.eps, self.fold_after = float(eps), int(fold_after)
         self.device = torch.device(device)
