@@ -138,10 +138,20 @@ def graph_steps(step, steps, batch=20):
     return ms, stats
 
 
+E2M3_SUFFIX = "_e2m3"  # a W4A4 workload with its 4-bit codes stored as FP6 E2M3 (code width 6)
+
+
+def load_workload(name):
+    import dataclasses
+    import synth
+    if name.endswith(E2M3_SUFFIX):
+        return dataclasses.replace(synth.make_workload(name[:-len(E2M3_SUFFIX)]), wbits=6, abits=6)
+    return synth.make_workload(name)
+
+
 def bench_prefill(name, steps, warmup):
     import torch
-    import synth
-    wl = synth.make_workload(name)
+    wl = load_workload(name)
     site = site_for(wl)
     x = site.upload(wl.x)
     res = site.upload(wl.residual) if wl.residual is not None else None
@@ -531,6 +541,8 @@ WORKLOAD_DESC = {
     "tiny_w8a8": "tiny 16-token site",
     "decode_m1_w8a8": "decode GEMV (fused gate+up), 1 token",
     "decode_m16_w8a8": "decode GEMV (fused gate+up), 16 tokens",
+    "gateup_w4a4_e2m3": "Gemma-2B-shaped MLP gate+up projection, 4-bit codes stored as FP6 E2M3 (FP6 MFMA)",
+    "down_w4a4_e2m3": "Gemma-2B-shaped MLP down projection with the residual, 4-bit codes stored as FP6 E2M3",
 }
 
 
@@ -637,7 +649,8 @@ def main():
     if not args.no_secondary:
         # the other 1024-token prefill shape (part of the headline metric), then the
         # W4A4 Gemma-shaped MLP sites (parity configs, reported for completeness)
-        for name in ("down_w8a8", "gateup_w4a4", "down_w4a4"):
+        for name in ("down_w8a8", "gateup_w4a4", "down_w4a4", "gateup_w4a4" + E2M3_SUFFIX,
+                     "down_w4a4" + E2M3_SUFFIX):
             s = bench_prefill(name, max(20, args.steps // 4), args.warmup)
             secondary.append({"workload": name, "metric": "fq_linear TOPS", "value": s["tops"],
                               "frac_int8_peak": s["tops"] / PEAK_INT8_TOPS, "ms_per_call": s["ms"],
