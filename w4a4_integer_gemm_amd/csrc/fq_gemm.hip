@@ -22,7 +22,9 @@
 //   - Waves 0/1 take tokens 0 .. BM/2-1 / BM/2 .. BM-1 and waves 0,1 / 2,3 take
 //     alternate 32-deep k steps of every stage (split k inside the workgroup),
 //     so each wave reads half the weight fragments a token-only split would.
-//     At the end the two k halves of a token block add up through LDS.
+//     At the end the two k halves of a token block add up through LDS.  On
+//     64-token tiles with a 4-bit operand waves 0/1 take the two halves of
+//     the rows instead, so that every unpacked fragment feeds two MFMAs.
 //   - A tile computes BNC rows (BNS rounded up to 32); rows past BNS belong to
 //     the next tile and are not stored.
 //   - Rows past M or N are clamped to the last row when loading (their results
@@ -31,9 +33,11 @@
 //     different XCDs, so tiles are renumbered to give each XCD a compact block
 //     of the output that shares operand rows in its own L2.
 //
-// k order inside a stage (lane l, MFMA k step j): k = 32 j + 16 (l / 32) + [0, 16).
-// A 4-bit operand's 16 codes are 8 bytes, unpacked to bytes in registers; an
-// 8-bit partner permutes its bytes into the nibble order of fq_device.h.
+// k order inside a stage (lane l, MFMA k step j): k = 32 j + 16 (l / 32) + [0, 16)
+// with 8-bit codes; with a 4-bit operand the steps go in pairs, step 2 p + e
+// taking k = 64 p + 32 (l / 32) + 16 e + [0, 16) (pair_offset below).  A 4-bit
+// operand's 16 codes are 8 bytes, unpacked to bytes in registers; an 8-bit
+// partner permutes its bytes into the nibble order of fq_device.h.
 #include <hip/hip_runtime.h>
 
 #include <cstring>
@@ -66,8 +70,13 @@ struct Cfg {
     static constexpr int C = CA + CW;
     static constexpr int STAGE = C * 1024;
     static constexpr int LDS = NS * STAGE;
-    static constexpr int TMF = BM / 64;   // 32-token fragments per wave
-    static constexpr int TN = BNC / 32;   // 32-row weight fragments per wave
+    // 32x32x32 form: the two wave pairs split the tokens (TMF fragments of 32
+    // per wave, all BNC rows); with a 4-bit operand on a 64-token tile they
+    // split the rows instead (RSPLIT: all tokens, BNC / 2 rows per wave), so
+    // that each unpacked weight fragment feeds two MFMAs
+    static constexpr bool RSPLIT = !MF16_ && KS == 256 && BM_ == 64 && BNC_ % 64 == 0;
+    static constexpr int TMF = RSPLIT ? BM / 32 : BM / 64;  // 32-token fragments per wave
+    static constexpr int TN = RSPLIT ? BNC / 64 : BNC / 32;  // 32-row weight fragments per wave
     static constexpr int TN0 = (TN + 1) / 2;  // output fragments stored by the k-half 0 wave
     static constexpr int NLO = C / 4, NHI = (C + 3) / 4;
     // MF16: v_mfma_i32_16x16x64_i8 instead of 32x32x32: rows in fragments of
@@ -164,6 +173,48 @@ struct LdsOperand<8, 8> {
     static constexpr bool kIdentity = true;
     __device__ __forceinline__ static raw load(const uint8_t* p) { return *reinterpret_cast<const v4i*>(p); }
     __device__ __forceinline__ static v4i expand(raw r) { return r; }
+};
+
+// 32x32x32 form with a 4-bit operand (stages of 256 k): the MFMA k steps go
+// in pairs.  Lane half h of pair p takes k = 64 p + 32 h + 16 e + [0, 16) in
+// step 2 p + e (any order of k serves, as long as both operands use it), so a
+// lane's 4-bit chunk of the pair is one whole 16-byte slot (e = 0 in its low
+// 8 bytes) and an 8-bit partner's chunk of each step is the slot after the
+// previous one.  Every LDS read of these stages is then a ds_read_b128, which
+// the slot swizzle keeps conflict-free; 8-byte reads of one k half put two
+// rows on every bank pair.
+template <int BITS, int R>
+__device__ __forceinline__ int pair_offset(int lane, int p, int e) {
+    const int rho = lane & 31, h = lane >> 5;
+    if (BITS == 4) return 16 * slot_of<R>(rho, 2 * p + h);
+    return 16 * slot_of<R>(rho, 4 * p + 2 * h + e);
+}
+
+// One lane's operand chunk of a step pair as read (`raw`) and one step of it as
+// the MFMA takes it (`expand`).
+template <int BITS, int PARTNER>
+struct PairOperand;
+template <int PARTNER>
+struct PairOperand<4, PARTNER> {
+    typedef uint4 raw;
+    __device__ __forceinline__ static raw load(const uint8_t* base, const int (&off)[2]) {
+        return *reinterpret_cast<const uint4*>(base + off[0]);
+    }
+    __device__ __forceinline__ static v4i expand(const raw& r, int e) {
+        return frag_from_nibbles(e ? make_uint2(r.z, r.w) : make_uint2(r.x, r.y));
+    }
+};
+template <>
+struct PairOperand<8, 4> {
+    struct raw {
+        uint4 lo, hi;
+    };
+    __device__ __forceinline__ static raw load(const uint8_t* base, const int (&off)[2]) {
+        return raw{*reinterpret_cast<const uint4*>(base + off[0]), *reinterpret_cast<const uint4*>(base + off[1])};
+    }
+    __device__ __forceinline__ static v4i expand(const raw& r, int e) {
+        return frag_from_bytes_nibble_order(e ? r.hi : r.lo);
+    }
 };
 
 // global source of 1 KB load q of an operand tile for `lane`: row rho of the
@@ -495,7 +546,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, int tiles_m, int ti
     } else {
         // ---------------------------------------------------------- MFMA waves
         // wave roles: tokens wm * BM/2 .. + BM/2 (TMF fragments of 32), all BNC
-        // weight rows (TN fragments), and the MFMA k steps j = 2 i + kh of every stage
+        // weight rows (TN fragments), and the MFMA k steps j = 2 i + kh of every
+        // stage; with RSPLIT all tokens and rows wm * BNC/2 .. + BNC/2
         const int wm = wave & 1;
         const int kh = wave >> 1;
         int offa[CF::NSTEP], offw[CF::NSTEP];
@@ -511,61 +563,147 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, int tiles_m, int ti
 #pragma unroll
             for (int f = 0; f < CF::TMF; ++f) acc[i][f] = v16i{};
 
-        typedef LdsOperand<ABITS, WBITS> OpA;
-        typedef LdsOperand<WBITS, ABITS> OpW;
-        typename OpA::raw fa[2][CF::TMF];  // two steps' operands, as read
-        typename OpW::raw fw[2][CF::TN];
-        auto read_frags = [&](int s, int i, int buf) {
-            const uint8_t* base = lds + (s % CF::NS) * CF::STAGE;
+        if constexpr (CF::KS == 256) {
+            // A 4-bit operand: the paired k order above.  Local pair t of a
+            // stage is pair p = 2 t + kh (the k halves alternate by pair).  At
+            // a pair's start its token fragments are expanded for both steps,
+            // which frees their registers for the next pair's read; in its
+            // second step each weight fragment's registers take the next pair's
+            // chunk as soon as they are expanded.  The stage's last pair waits
+            // for this wave's reads after its first step and passes the barrier
+            // that frees the stage's slot and publishes the next stage, whose
+            // first pair it then reads.  A half-deep last stage is one pair per
+            // wave and has no barrier.
+            constexpr int NP = CF::NSTEP / 2;  // pairs per wave in a full stage
+            typedef PairOperand<ABITS, WBITS> PA;
+            typedef PairOperand<WBITS, ABITS> PW;
+            int pa[NP][2], pw[NP][2];
 #pragma unroll
-            for (int f = 0; f < CF::TMF; ++f) fa[buf][f] = OpA::load(base + offa[i] + f * 32 * CF::RA);
+            for (int t = 0; t < NP; ++t)
 #pragma unroll
-            for (int n = 0; n < CF::TN; ++n) fw[buf][n] = OpW::load(base + offw[i] + n * 32 * CF::RW);
-        };
-
-        barrier_nofence();  // stage 0 published
-        read_frags(0, 0, 0);
-
-        // One k stage.  In each step the first TMF MFMAs run on operands read
-        // one step earlier (expanded at the step's start); then the next step's
-        // operands are read from LDS (their latency hides behind the remaining
-        // MFMAs).  Before the last
-        // step this wave's reads of the stage are waited for and the barrier
-        // both frees the stage's slot and publishes the next stage.  A
-        // half-deep last stage (FULL = false) runs its first NSTEP/2 steps and
-        // has no barrier.
-        auto stage = [&](int s, auto full_tag) {
-            constexpr bool kFull = decltype(full_tag)::value;
-            constexpr int kSteps = kFull ? CF::NSTEP : CF::NSTEP / 2;
-            const int next = s + 1 < nk ? s + 1 : nk - 1;
-#pragma unroll
-            for (int j = 0; j < kSteps; ++j) {
-                const int cur = j & 1;
-                v4i xa[CF::TMF];  // this step's token fragments, expanded
-#pragma unroll
-                for (int f = 0; f < CF::TMF; ++f) xa[f] = OpA::expand(fa[cur][f]);
-                const v4i w0 = OpW::expand(fw[cur][0]);
-#pragma unroll
-                for (int f = 0; f < CF::TMF; ++f) acc[0][f] = mfma32x32x32(w0, xa[f], acc[0][f]);
-                __builtin_amdgcn_sched_barrier(0);
-                if (j + 1 < kSteps) {
-                    read_frags(s, j + 1, cur ^ 1);
-                } else if (kFull) {
-                    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-                    barrier_nofence();
-                    read_frags(next, 0, cur ^ 1);
+                for (int e = 0; e < 2; ++e) {
+                    pa[t][e] = pair_offset<ABITS, CF::RA>(lane, 2 * t + kh, e) +
+                               (CF::RSPLIT ? 0 : wm * CF::TMF * 32 * CF::RA);
+                    pw[t][e] = pair_offset<WBITS, CF::RW>(lane, 2 * t + kh, e) + CF::CA * 1024 +
+                               (CF::RSPLIT ? wm * CF::TN * 32 * CF::RW : 0);
                 }
-                __builtin_amdgcn_sched_barrier(0);
+            typename PA::raw ra[CF::TMF];
+            typename PW::raw rw[CF::TN];
+            auto read_a = [&](int s, int t) {
+                const uint8_t* base = lds + (s % CF::NS) * CF::STAGE;
 #pragma unroll
-                for (int n = 1; n < CF::TN; ++n) {
-                    const v4i w = OpW::expand(fw[cur][n]);
+                for (int f = 0; f < CF::TMF; ++f) ra[f] = PA::load(base + f * 32 * CF::RA, pa[t]);
+            };
+            auto read_w = [&](int s, int t, int n) {
+                rw[n] = PW::load(lds + (s % CF::NS) * CF::STAGE + n * 32 * CF::RW, pw[t]);
+            };
+            barrier_nofence();  // stage 0 published
+            read_a(0, 0);
 #pragma unroll
-                    for (int f = 0; f < CF::TMF; ++f) acc[n][f] = mfma32x32x32(w, xa[f], acc[n][f]);
+            for (int n = 0; n < CF::TN; ++n) read_w(0, 0, n);
+            auto stage = [&](int s, auto full_tag) {
+                constexpr bool kFull = decltype(full_tag)::value;
+                constexpr int kPairs = kFull ? NP : NP / 2;
+                const int next = s + 1 < nk ? s + 1 : nk - 1;
+#pragma unroll
+                for (int t = 0; t < kPairs; ++t) {
+                    const bool last = t + 1 == kPairs;
+                    v4i xa[2][CF::TMF];
+#pragma unroll
+                    for (int f = 0; f < CF::TMF; ++f) {
+                        xa[0][f] = PA::expand(ra[f], 0);
+                        xa[1][f] = PA::expand(ra[f], 1);
+                    }
+                    if (!last) read_a(s, t + 1);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int n = 0; n < CF::TN; ++n) {
+                        const v4i w = PW::expand(rw[n], 0);
+#pragma unroll
+                        for (int f = 0; f < CF::TMF; ++f) acc[n][f] = mfma32x32x32(w, xa[0][f], acc[n][f]);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (last && kFull) {
+                        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave is done with stage s
+                        barrier_nofence();
+                        read_a(next, 0);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int n = 0; n < CF::TN; ++n) {
+                        const v4i w = PW::expand(rw[n], 1);
+                        if (!last)
+                            read_w(s, t + 1, n);
+                        else if (kFull)
+                            read_w(next, 0, n);
+#pragma unroll
+                        for (int f = 0; f < CF::TMF; ++f) acc[n][f] = mfma32x32x32(w, xa[1][f], acc[n][f]);
+                        // (each read goes out with its fragment's step: grouped at
+                        // the step's end they left the next pair waiting for them)
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-            }
-        };
-        for (int s = 0; s < nfull; ++s) stage(s, std::true_type{});
-        if (half_last) stage(nk - 1, std::false_type{});
+            };
+            for (int s = 0; s < nfull; ++s) stage(s, std::true_type{});
+            if (half_last) stage(nk - 1, std::false_type{});
+        } else {
+            typedef LdsOperand<ABITS, WBITS> OpA;
+            typedef LdsOperand<WBITS, ABITS> OpW;
+            typename OpA::raw fa[2][CF::TMF];  // two steps' operands, as read
+            typename OpW::raw fw[2][CF::TN];
+            auto read_frags = [&](int s, int i, int buf) {
+                const uint8_t* base = lds + (s % CF::NS) * CF::STAGE;
+    #pragma unroll
+                for (int f = 0; f < CF::TMF; ++f) fa[buf][f] = OpA::load(base + offa[i] + f * 32 * CF::RA);
+    #pragma unroll
+                for (int n = 0; n < CF::TN; ++n) fw[buf][n] = OpW::load(base + offw[i] + n * 32 * CF::RW);
+            };
+
+            barrier_nofence();  // stage 0 published
+            read_frags(0, 0, 0);
+
+            // One k stage.  In each step the first TMF MFMAs run on operands read
+            // one step earlier (expanded at the step's start); then the next step's
+            // operands are read from LDS (their latency hides behind the remaining
+            // MFMAs).  Before the last
+            // step this wave's reads of the stage are waited for and the barrier
+            // both frees the stage's slot and publishes the next stage.  A
+            // half-deep last stage (FULL = false) runs its first NSTEP/2 steps and
+            // has no barrier.
+            auto stage = [&](int s, auto full_tag) {
+                constexpr bool kFull = decltype(full_tag)::value;
+                constexpr int kSteps = kFull ? CF::NSTEP : CF::NSTEP / 2;
+                const int next = s + 1 < nk ? s + 1 : nk - 1;
+    #pragma unroll
+                for (int j = 0; j < kSteps; ++j) {
+                    const int cur = j & 1;
+                    v4i xa[CF::TMF];  // this step's token fragments, expanded
+    #pragma unroll
+                    for (int f = 0; f < CF::TMF; ++f) xa[f] = OpA::expand(fa[cur][f]);
+                    const v4i w0 = OpW::expand(fw[cur][0]);
+    #pragma unroll
+                    for (int f = 0; f < CF::TMF; ++f) acc[0][f] = mfma32x32x32(w0, xa[f], acc[0][f]);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (j + 1 < kSteps) {
+                        read_frags(s, j + 1, cur ^ 1);
+                    } else if (kFull) {
+                        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+                        barrier_nofence();
+                        read_frags(next, 0, cur ^ 1);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+                    for (int n = 1; n < CF::TN; ++n) {
+                        const v4i w = OpW::expand(fw[cur][n]);
+    #pragma unroll
+                        for (int f = 0; f < CF::TMF; ++f) acc[n][f] = mfma32x32x32(w, xa[f], acc[n][f]);
+                    }
+                }
+            };
+            for (int s = 0; s < nfull; ++s) stage(s, std::true_type{});
+            if (half_last) stage(nk - 1, std::false_type{});
+        }
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's ring reads are done
         load_epilogue_operands();
         barrier_nofence();                   // E1: the ring is idle
@@ -574,11 +712,13 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, int tiles_m, int ti
         // ring: the k-half 1 waves write their partial sums, then the k-half 0
         // waves add theirs.  Lane l holds token wm BM/2 + 32 f + l % 32 and rows
         // 32 n + 8 q + 4 (l / 32) + [0, 4) of fragment (n, f) in registers 4 q ...
+        // (with RSPLIT token 32 f + l % 32 and rows wm BNC/2 + 32 n + ...)
         int32_t* X = reinterpret_cast<int32_t*>(lds);
         constexpr int XS = acc_stride<CF>();
         auto xrow = [&](int f, int n, int q) {
-            const int m = wm * (CF::BM / 2) + 32 * f + (lane & 31);
-            return reinterpret_cast<v4i*>(X + m * XS + 32 * n + 8 * q + 4 * (lane >> 5));
+            const int m = (CF::RSPLIT ? 0 : wm * (CF::BM / 2)) + 32 * f + (lane & 31);
+            const int col = (CF::RSPLIT ? wm * CF::TN * 32 : 0) + 32 * n + 8 * q + 4 * (lane >> 5);
+            return reinterpret_cast<v4i*>(X + m * XS + col);
         };
         if (kh == 1) {
 #pragma unroll
