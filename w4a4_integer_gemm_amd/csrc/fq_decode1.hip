@@ -44,7 +44,7 @@ constexpr int kRows = 2;  // groups of 16 weight rows per workgroup
 constexpr int kMaxK = kWaves * 64 * kE;
 
 template <int ABITS, int WBITS, bool NORM, int AMODE, int LOG2B, int PER>
-__global__ __launch_bounds__(64 * kWaves) void decode1_kernel(PrologueArgs p, GemmArgs g, float rs) {
+__global__ __launch_bounds__(64 * kWaves) void decode1_kernel(PrologueArgs p, GemmArgs g, TokenConsts tc) {
     using U = Unit<ABITS, WBITS>;
     __shared__ double red_d[kWaves];
     __shared__ float red_f[kWaves];
@@ -81,7 +81,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode1_kernel(PrologueArgs p, Ge
     uint8_t* const ws_codes = p.codes;
     const bool first = blockIdx.x == 0;
     const float s = quantise_loaded<kE, ABITS, NORM, AMODE, LOG2B>(
-        t, K, p.gamma, p.eps, p.ascale, rs, tid, kWaves, red_d, red_f, [&](int off, auto v) {
+        t, K, p.gamma, p.eps, p.ascale, tc, tid, kWaves, red_d, red_f, [&](int off, auto v) {
             *reinterpret_cast<decltype(v)*>(act_lds + off) = v;
             if (first) *reinterpret_cast<decltype(v)*>(ws_codes + off) = v;
         });
@@ -126,23 +126,23 @@ __global__ __launch_bounds__(64 * kWaves) void decode1_kernel(PrologueArgs p, Ge
 
 template <int ABITS, int WBITS, bool NORM, int AMODE, int LOG2B>
 hipError_t launch_per(const PrologueArgs& p, const GemmArgs& g, int per, hipStream_t st) {
-    const float rs = float(1.0 / std::sqrt(double(p.hblock)));
+    const TokenConsts tc{float(1.0 / std::sqrt(double(p.hblock))), 1.0 / double(p.K)};
     const dim3 grid((g.N + 16 * kRows - 1) / (16 * kRows)), block(64 * kWaves);
     // PER: units per wave in registers, rounded up to 4 or 8, with 7 exact for
     // 8-bit codes (the 3584-wide layers: 56 units over 8 waves; one unit
     // repeated there measured 27.3 against 27.0 us)
     if (per <= 4) {
-        hipLaunchKernelGGL((decode1_kernel<ABITS, WBITS, NORM, AMODE, LOG2B, 4>), grid, block, 0, st, p, g, rs);
+        hipLaunchKernelGGL((decode1_kernel<ABITS, WBITS, NORM, AMODE, LOG2B, 4>), grid, block, 0, st, p, g, tc);
         return hipGetLastError();
     }
     if constexpr (ABITS == 8 && WBITS == 8) {
         if (per == 7) {
             hipLaunchKernelGGL((decode1_kernel<ABITS, WBITS, NORM, AMODE, LOG2B, 7>), grid, block, 0, st, p, g,
-                               rs);
+                               tc);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((decode1_kernel<ABITS, WBITS, NORM, AMODE, LOG2B, 8>), grid, block, 0, st, p, g, rs);
+    hipLaunchKernelGGL((decode1_kernel<ABITS, WBITS, NORM, AMODE, LOG2B, 8>), grid, block, 0, st, p, g, tc);
     return hipGetLastError();
 }
 

@@ -56,7 +56,7 @@ constexpr int kMaxWaves = kMaxThreads / 64;
 template <int E, int ABITS, bool NORM, int AMODE, int LOG2B>
 __global__ __launch_bounds__(kMaxThreads) void prologue_kernel(const uint16_t* __restrict__ x, int K, int64_t ldx,
                                                                 const float* __restrict__ gamma, float eps,
-                                                                const float* __restrict__ ascale, float rs,
+                                                                const float* __restrict__ ascale, TokenConsts tc,
                                                                 uint8_t* __restrict__ codes,
                                                                 float* __restrict__ act_scale) {
     // A lane's codes (E * ABITS / 8 bytes) leave in one store when they are at
@@ -74,7 +74,7 @@ __global__ __launch_bounds__(kMaxThreads) void prologue_kernel(const uint16_t* _
     const int c = threadIdx.x;
     uint8_t* const row = codes + int64_t(m) * (ABITS == 8 ? K : ABITS == 6 ? K / 4 * 3 : K / 2);
     const float s = quantise_token<E, ABITS, NORM, AMODE, LOG2B>(
-        x + int64_t(m) * ldx, K, gamma, eps, ascale, rs, c, int(blockDim.x) >> 6, red_d, red_f,
+        x + int64_t(m) * ldx, K, gamma, eps, ascale, tc, c, int(blockDim.x) >> 6, red_d, red_f,
         [&](int off, auto v) {
             if constexpr (kWriteThrough) {
                 if constexpr (sizeof(v) == 16)
@@ -91,45 +91,45 @@ __global__ __launch_bounds__(kMaxThreads) void prologue_kernel(const uint16_t* _
 }
 
 template <int E, int ABITS, bool NORM, int AMODE, int LOG2B>
-hipError_t launch_e(dim3 grid, dim3 block, hipStream_t st, const PrologueArgs& a, float rs) {
+hipError_t launch_e(dim3 grid, dim3 block, hipStream_t st, const PrologueArgs& a, TokenConsts tc) {
     if constexpr ((1 << LOG2B) > 16 * E || (ABITS == 6 && E < 16)) {
         return hipErrorInvalidValue;  // not chosen by launch_prologue
     } else {
         hipLaunchKernelGGL((prologue_kernel<E, ABITS, NORM, AMODE, LOG2B>), grid, block, 0, st, a.x, a.K, a.ldx,
-                           a.gamma, a.eps, a.ascale, rs, a.codes, a.act_scale);
+                           a.gamma, a.eps, a.ascale, tc, a.codes, a.act_scale);
         return hipGetLastError();
     }
 }
 
 template <int E, int ABITS, bool NORM, int AMODE>
-hipError_t launch_b(int log2b, dim3 grid, dim3 block, hipStream_t st, const PrologueArgs& a, float rs) {
+hipError_t launch_b(int log2b, dim3 grid, dim3 block, hipStream_t st, const PrologueArgs& a, TokenConsts tc) {
     switch (log2b) {
-        case 0: return launch_e<E, ABITS, NORM, AMODE, 0>(grid, block, st, a, rs);
-        case 1: return launch_e<E, ABITS, NORM, AMODE, 1>(grid, block, st, a, rs);
-        case 2: return launch_e<E, ABITS, NORM, AMODE, 2>(grid, block, st, a, rs);
-        case 3: return launch_e<E, ABITS, NORM, AMODE, 3>(grid, block, st, a, rs);
-        case 4: return launch_e<E, ABITS, NORM, AMODE, 4>(grid, block, st, a, rs);
-        case 5: return launch_e<E, ABITS, NORM, AMODE, 5>(grid, block, st, a, rs);
-        case 6: return launch_e<E, ABITS, NORM, AMODE, 6>(grid, block, st, a, rs);
-        case 7: return launch_e<E, ABITS, NORM, AMODE, 7>(grid, block, st, a, rs);
-        case 8: return launch_e<E, ABITS, NORM, AMODE, 8>(grid, block, st, a, rs);
+        case 0: return launch_e<E, ABITS, NORM, AMODE, 0>(grid, block, st, a, tc);
+        case 1: return launch_e<E, ABITS, NORM, AMODE, 1>(grid, block, st, a, tc);
+        case 2: return launch_e<E, ABITS, NORM, AMODE, 2>(grid, block, st, a, tc);
+        case 3: return launch_e<E, ABITS, NORM, AMODE, 3>(grid, block, st, a, tc);
+        case 4: return launch_e<E, ABITS, NORM, AMODE, 4>(grid, block, st, a, tc);
+        case 5: return launch_e<E, ABITS, NORM, AMODE, 5>(grid, block, st, a, tc);
+        case 6: return launch_e<E, ABITS, NORM, AMODE, 6>(grid, block, st, a, tc);
+        case 7: return launch_e<E, ABITS, NORM, AMODE, 7>(grid, block, st, a, tc);
+        case 8: return launch_e<E, ABITS, NORM, AMODE, 8>(grid, block, st, a, tc);
         default: return hipErrorInvalidValue;
     }
 }
 
 template <int E, int ABITS>
-hipError_t launch_modes(dim3 grid, dim3 block, hipStream_t st, const PrologueArgs& a, float rs) {
+hipError_t launch_modes(dim3 grid, dim3 block, hipStream_t st, const PrologueArgs& a, TokenConsts tc) {
     int log2b = 0;
     while ((1 << log2b) < a.hblock) ++log2b;
     const int amode = a.ascale ? (a.fold_after ? 2 : 1) : 0;
     if (a.gamma) {
-        if (amode == 0) return launch_b<E, ABITS, true, 0>(log2b, grid, block, st, a, rs);
-        if (amode == 1) return launch_b<E, ABITS, true, 1>(log2b, grid, block, st, a, rs);
-        return launch_b<E, ABITS, true, 2>(log2b, grid, block, st, a, rs);
+        if (amode == 0) return launch_b<E, ABITS, true, 0>(log2b, grid, block, st, a, tc);
+        if (amode == 1) return launch_b<E, ABITS, true, 1>(log2b, grid, block, st, a, tc);
+        return launch_b<E, ABITS, true, 2>(log2b, grid, block, st, a, tc);
     }
-    if (amode == 0) return launch_b<E, ABITS, false, 0>(log2b, grid, block, st, a, rs);
-    if (amode == 1) return launch_b<E, ABITS, false, 1>(log2b, grid, block, st, a, rs);
-    return launch_b<E, ABITS, false, 2>(log2b, grid, block, st, a, rs);
+    if (amode == 0) return launch_b<E, ABITS, false, 0>(log2b, grid, block, st, a, tc);
+    if (amode == 1) return launch_b<E, ABITS, false, 1>(log2b, grid, block, st, a, tc);
+    return launch_b<E, ABITS, false, 2>(log2b, grid, block, st, a, tc);
 }
 
 }  // namespace
@@ -149,21 +149,21 @@ hipError_t launch_prologue(const PrologueArgs& a, hipStream_t stream) {
     const int nlanes = a.K / E;
     const int T = (nlanes + 63) / 64 * 64;
     if (T > kMaxThreads) return hipErrorInvalidValue;
-    const float rs = float(1.0 / std::sqrt(double(a.hblock)));
+    const TokenConsts tc{float(1.0 / std::sqrt(double(a.hblock))), 1.0 / double(a.K)};
     dim3 grid(a.M), block(T);
     if (E == 8)
-        return a.abits == 8 ? launch_modes<8, 8>(grid, block, stream, a, rs) : launch_modes<8, 4>(grid, block, stream, a, rs);
+        return a.abits == 8 ? launch_modes<8, 8>(grid, block, stream, a, tc) : launch_modes<8, 4>(grid, block, stream, a, tc);
     if (E == 16)
-        return a.abits == 8   ? launch_modes<16, 8>(grid, block, stream, a, rs)
-               : a.abits == 6 ? launch_modes<16, 6>(grid, block, stream, a, rs)
-                              : launch_modes<16, 4>(grid, block, stream, a, rs);
+        return a.abits == 8   ? launch_modes<16, 8>(grid, block, stream, a, tc)
+               : a.abits == 6 ? launch_modes<16, 6>(grid, block, stream, a, tc)
+                              : launch_modes<16, 4>(grid, block, stream, a, tc);
     if (E == 32)
-        return a.abits == 8   ? launch_modes<32, 8>(grid, block, stream, a, rs)
-               : a.abits == 6 ? launch_modes<32, 6>(grid, block, stream, a, rs)
-                              : launch_modes<32, 4>(grid, block, stream, a, rs);
-    return a.abits == 8   ? launch_modes<64, 8>(grid, block, stream, a, rs)
-           : a.abits == 6 ? launch_modes<64, 6>(grid, block, stream, a, rs)
-                          : launch_modes<64, 4>(grid, block, stream, a, rs);
+        return a.abits == 8   ? launch_modes<32, 8>(grid, block, stream, a, tc)
+               : a.abits == 6 ? launch_modes<32, 6>(grid, block, stream, a, tc)
+                              : launch_modes<32, 4>(grid, block, stream, a, tc);
+    return a.abits == 8   ? launch_modes<64, 8>(grid, block, stream, a, tc)
+           : a.abits == 6 ? launch_modes<64, 6>(grid, block, stream, a, tc)
+                          : launch_modes<64, 4>(grid, block, stream, a, tc);
 }
 
 }  // namespace fq

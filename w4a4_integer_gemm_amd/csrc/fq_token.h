@@ -13,6 +13,14 @@
 
 namespace fq {
 
+// Per-launch constants of a token's arithmetic, computed on the host in
+// float64 and correctly rounded: rs = 1/sqrt(b) (float) and rk = 1/K (the
+// mean's divide, below).
+struct TokenConsts {
+    float rs;
+    double rk;
+};
+
 // Whole-wave reductions on the VALU: DPP within rows of 16 lanes (xor 1,
 // xor 2, half-row mirror, row mirror), then the gfx950 row swaps (lanes
 // l <-> l ^ 16 and l <-> l ^ 32).  Each step combines two complete partial
@@ -22,15 +30,20 @@ __device__ __forceinline__ int dpp_i(int v) {
     return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-    v = fmaxf(v, __int_as_float(dpp_i<0xB1>(__float_as_int(v))));   // quad_perm [1,0,3,2]
-    v = fmaxf(v, __int_as_float(dpp_i<0x4E>(__float_as_int(v))));   // quad_perm [2,3,0,1]
-    v = fmaxf(v, __int_as_float(dpp_i<0x141>(__float_as_int(v))));  // row_half_mirror
-    v = fmaxf(v, __int_as_float(dpp_i<0x140>(__float_as_int(v))));  // row_mirror
-    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
-    v = fmaxf(__int_as_float(a[0]), __int_as_float(a[1]));
-    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
-    return fmaxf(__int_as_float(b[0]), __int_as_float(b[1]));
+// Maximum over the wave of a value that is >= 0 and not NaN: for such floats
+// the order of the bit patterns as unsigned integers is the order of the
+// values, and the integer max needs none of the quieting maxes that fmaxf
+// compiles to here.
+__device__ __forceinline__ float wave_max_nonneg(float x) {
+    uint32_t v = __float_as_uint(x);
+    v = max(v, uint32_t(dpp_i<0xB1>(int(v))));   // quad_perm [1,0,3,2]
+    v = max(v, uint32_t(dpp_i<0x4E>(int(v))));   // quad_perm [2,3,0,1]
+    v = max(v, uint32_t(dpp_i<0x141>(int(v))));  // row_half_mirror
+    v = max(v, uint32_t(dpp_i<0x140>(int(v))));  // row_mirror
+    const auto a = __builtin_amdgcn_permlane16_swap(int(v), int(v), false, false);
+    v = max(uint32_t(a[0]), uint32_t(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(int(v), int(v), false, false);
+    return __uint_as_float(max(uint32_t(b[0]), uint32_t(b[1])));
 }
 
 template <int CTRL>
@@ -181,16 +194,27 @@ __device__ __forceinline__ double lane_sumsq(const float (&v)[E]) {
     return t[0];
 }
 
+// max(|a|, |b|, c) in one v_max3_f32 with |.| source modifiers (fmaxf of
+// fabsf compiled to an extra quieting max per value).  Like fmaxf it returns
+// the other operands where one is a quiet NaN, so with c = 0 the result is
+// never NaN.
+__device__ __forceinline__ float max3_abs(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, |%1|, |%2|, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
+// max |v_i| over a lane's values, in two interleaved chains; >= 0, not NaN
 template <int E>
 __device__ __forceinline__ float lane_absmax(const float (&v)[E]) {
-    float t[E / 2];
+    static_assert(E % 4 == 0, "values in groups of four");
+    float m0 = max3_abs(v[0], v[1], 0.0f), m1 = max3_abs(v[2], v[3], 0.0f);
 #pragma unroll
-    for (int i = 0; i < E / 2; ++i) t[i] = fmaxf(fabsf(v[2 * i]), fabsf(v[2 * i + 1]));
-#pragma unroll
-    for (int w = E / 4; w >= 1; w >>= 1)
-#pragma unroll
-        for (int i = 0; i < w; ++i) t[i] = fmaxf(t[i], t[i + w]);
-    return t[0];
+    for (int i = 4; i < E; i += 4) {
+        m0 = max3_abs(v[i], v[i + 1], m0);
+        m1 = max3_abs(v[i + 2], v[i + 3], m1);
+    }
+    return __uint_as_float(max(__float_as_uint(m0), __float_as_uint(m1)));
 }
 
 // Adding 1.5 * 2^23 to |q| <= 2^22 rounds q to an integer, ties to even (the
@@ -255,7 +279,7 @@ __device__ __forceinline__ TokenLoad<E, NORM> load_token_clamped(const uint16_t*
 // nwaves-entry LDS scratch for the cross-wave reductions.
 template <int E, int ABITS, bool NORM, int AMODE, int LOG2B, class Store>
 __device__ __forceinline__ float quantise_loaded(const TokenLoad<E, NORM>& t, int K, const float* __restrict__ gamma,
-                                                 float eps, const float* __restrict__ ascale, float rs, int c,
+                                                 float eps, const float* __restrict__ ascale, TokenConsts tc, int c,
                                                  int nwaves, double* red_d, float* red_f, Store store) {
     constexpr int hblock = 1 << LOG2B;
     static_assert(hblock <= 16 * E, "a Hadamard block spans at most 16 lanes (cross-lane distances 1 .. 8)");
@@ -280,7 +304,10 @@ __device__ __forceinline__ float quantise_loaded(const TokenLoad<E, NORM>& t, in
             ss = 0.0;
             for (int w = 0; w < nwaves; ++w) ss += red_d[w];
         }
-        const float ms = float(ss / double(K));
+        // ss / K correctly rounded in float64 without a divide: Markstein's
+        // correction of ss * RN(1/K) (the remainder is exact in an fma)
+        const double q0 = ss * tc.rk;
+        const float ms = float(__builtin_fma(__builtin_fma(-q0, double(K), ss), tc.rk, q0));
         const float rinv = 1.0f / sqrtf(ms + eps);
         if (active) {
 #pragma unroll
@@ -317,23 +344,32 @@ __device__ __forceinline__ float quantise_loaded(const TokenLoad<E, NORM>& t, in
     if constexpr (hblock > 8 * E) cross_stage<8, E>(v, lane);
     // the cross stages' sign: -1 for an odd number of set lane bits among those they used
     constexpr int kCrossBits = hblock > E ? hblock / E - 1 : 0;
-    const float rs_lane = (__builtin_popcount(lane & kCrossBits) & 1) ? -rs : rs;
+    const float rs_lane = (__builtin_popcount(lane & kCrossBits) & 1) ? -tc.rs : tc.rs;
 #pragma unroll
     for (int i = 0; i < E; ++i) v[i] = v[i] * rs_lane;
 
     if (AMODE == 2) divide_by_vector<E>(v, ascale, c, active);
 
     // per-token amax (lanes past K hold zeros)
-    float amax = wave_max(active ? lane_absmax<E>(v) : 0.0f);
+    float amax = wave_max_nonneg(active ? lane_absmax<E>(v) : 0.0f);
     if (nwaves > 1) {
         if (lane == 0) red_f[wave] = amax;
         __syncthreads();
-        amax = 0.0f;
-        for (int w = 0; w < nwaves; ++w) amax = fmaxf(amax, red_f[w]);
+        uint32_t m = 0;
+        for (int w = 0; w < nwaves; ++w) m = max(m, __float_as_uint(red_f[w]));
+        amax = __uint_as_float(m);
     }
-    const float s = amax / float(qmax);
-    const bool fast = s >= 0x1p-100f && s <= 0x1p+100f;
-    const float r = fast ? 1.0f / s : 0.0f;
+    // s = amax / qmax, correctly rounded: Markstein's correction of
+    // amax * RN(1/qmax) equals the IEEE quotient for every finite amax >= 0
+    // (checked exhaustively for both qmax); a token outside the fast range,
+    // or with a non-finite amax, divides below.  (fast is the same in every
+    // lane; taken from lane 0 it is a scalar branch.)
+    constexpr float rq = 1.0f / float(qmax);
+    const float s0 = amax * rq;
+    float s = __builtin_fmaf(__builtin_fmaf(-s0, float(qmax), amax), rq, s0);
+    const bool fast = __builtin_amdgcn_readfirstlane(int(s >= 0x1p-100f && s <= 0x1p+100f)) != 0;
+
+    float r = 0.0f;
 
     // Codes.  |h| <= amax and s is amax / qmax rounded, so |h / s| stays below
     // qmax + 1/2 and round-half-even never leaves [-qmax, qmax]: the clamp of
@@ -413,11 +449,12 @@ __device__ __forceinline__ float quantise_loaded(const TokenLoad<E, NORM>& t, in
             }
         }
     };
-    if (active) {
-        if (fast)
-            quantise(std::true_type{});
-        else
-            quantise(std::false_type{});
+    if (fast) {
+        r = 1.0f / s;
+        if (active) quantise(std::true_type{});
+    } else {
+        s = amax / float(qmax);
+        if (active) quantise(std::false_type{});
     }
     return s;
 }
@@ -425,10 +462,10 @@ __device__ __forceinline__ float quantise_loaded(const TokenLoad<E, NORM>& t, in
 template <int E, int ABITS, bool NORM, int AMODE, int LOG2B, class Store>
 __device__ __forceinline__ float quantise_token(const uint16_t* __restrict__ xr, int K,
                                                 const float* __restrict__ gamma, float eps,
-                                                const float* __restrict__ ascale, float rs, int c, int nwaves,
+                                                const float* __restrict__ ascale, TokenConsts tc, int c, int nwaves,
                                                 double* red_d, float* red_f, Store store) {
     return quantise_loaded<E, ABITS, NORM, AMODE, LOG2B>(load_token<E, NORM>(xr, K, gamma, c), K, gamma, eps,
-                                                         ascale, rs, c, nwaves, red_d, red_f, store);
+                                                         ascale, tc, c, nwaves, red_d, red_f, store);
 }
 
 }  // namespace fq
