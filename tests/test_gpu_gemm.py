@@ -77,7 +77,9 @@ def test_gemm_strided_output_and_residual():
 
 
 def _tile_case(tile, bits):
-    for M, N, K in ((300, 392, 768), (33, 1000, 1280)):
+    # (97, 264, 1408): with a 4-bit operand, five full 256-deep stages and a
+    # half-deep last one
+    for M, N, K in ((300, 392, 768), (33, 1000, 1280), (97, 264, 1408)):
         acc, acc_ref, yg, yf, sa, sw, b, res = run_gemm(M, N, K, bits[0], bits[1], seed=M + N, bias=True,
                                                         residual=True)
         assert np.array_equal(acc, acc_ref), f"{tile}: {np.count_nonzero(acc != acc_ref)} accumulators differ"
@@ -88,7 +90,8 @@ def _tile_case(tile, bits):
 @pytest.mark.parametrize("bits", [(8, 8), (4, 4), (8, 4), (4, 8)], ids=lambda b: "A{}W{}".format(*b))
 def test_gemm_every_tile_shape(tile, bits, hook):
     """Each tile shape of the MFMA kernel (forced through the gemm_tile test hook)
-    on a ragged problem: M and N not multiples of the tile, several k stages."""
+    on ragged problems: M and N not multiples of the tile, several k stages, and
+    a half-deep last stage for 4-bit operands."""
     hook(f"gemm_tile={tile}")
     log(f"gemm tile {tile} bits {bits}")
     _tile_case(tile, bits)
