@@ -56,11 +56,14 @@ class DeviceSite:
         self.ascale = _to_dev(self.ascale_host, self.device)
         self.bias = _to_dev(None if bias is None else np.ascontiguousarray(bias, np.float32), self.device)
         self._ws = None
+        self._ws_bytes = {}  # M -> fq_linear_workspace_bytes
 
     # -- buffers
     def workspace(self, M: int):
         import torch
-        nbytes = B.fq_linear_workspace_bytes(M, self.K, self.abits)
+        nbytes = self._ws_bytes.get(M)
+        if nbytes is None:
+            nbytes = self._ws_bytes[M] = B.fq_linear_workspace_bytes(M, self.K, self.abits)
         if self._ws is None or self._ws.numel() < nbytes:
             self._ws = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
         return self._ws
