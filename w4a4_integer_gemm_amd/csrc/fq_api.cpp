@@ -150,8 +150,9 @@ fq_status check_bits(const char* fn, const char* name, int32_t bits) {
     return FQ_OK;
 }
 
-// K bounds; `mult` is the granularity the entry point needs (8 for the
-// prologue's 32-value lanes, 128 for the GEMM's k stages).
+// K bounds; `mult` is the granularity the entry point needs (32 for the
+// prologue, whose lanes hold up to 32 values each below K = 32768; 128 for the
+// GEMM's k stages).
 fq_status check_k(const char* fn, int32_t K, int32_t mult) {
     if (K < mult || K > kMaxK)
         return fail(FQ_ERR_SHAPE, fmt("%s: K=%d outside [%d, %d]", fn, K, mult, kMaxK));
