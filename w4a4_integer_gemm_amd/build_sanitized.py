@@ -26,7 +26,11 @@ LIB = os.path.join(HERE, "libfq_san.so")
 ORACLE_LIB = os.path.join(ROOT, "oracle", "liboracle_san.so")
 SAN = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g"]
 HOST_SOURCES = ["fq_api.cpp", "fq_pack.cpp"]
-DEVICE_OBJECTS = ["fq_prologue.o", "fq_gemm.o", "fq_gemv.o", "fq_geglu.o", "fq_noalloc.o", "fq_decode1.o"]
+# the library's kernels, as the ordinary build compiled them (its list of sources)
+sys.path.insert(0, ROOT)
+from w4a4_integer_gemm_amd.build import SOURCES as _LIB_SOURCES  # noqa: E402
+
+DEVICE_OBJECTS = [os.path.splitext(s)[0] + ".o" for s in _LIB_SOURCES if s.endswith(".hip")]
 TESTS = ["tests/test_abi_cpu.py", "tests/test_oracle_pins.py", "tests/test_fold_consistency.py"]
 
 
